@@ -1,0 +1,201 @@
+/*
+ * santa.h -- C ABI of the SANTA decode-step attention library (libsanta.so).
+ *
+ * SANTA ("Stochastic Sparse Attention for Memory-Bound Inference", Lee et al.)
+ * replaces the value stage of decode attention by sampling:
+ *
+ *   s_i = q . k_i / sqrt(d)              exact scores over the whole cache (§2, Eq. 1)
+ *   p   = softmax(s)                     the post-softmax row as a categorical law (§2)
+ *   i_1..i_S ~ p                         multinomial (i.i.d.), stratified or
+ *                                        systematic draws (§2, Eq. 3; §2.1)
+ *   o   = (1/S) * sum_s v_{i_s}          gather-and-add of only the sampled V rows
+ *                                        (§2, Eq. 2-3), an unbiased estimate of A V
+ *                                        (Appendix A.1, A.4)
+ *
+ * The library computes this for one decode step of a batch of sequences with
+ * grouped-query attention (G = Hq / Hkv query heads share one KV head), on one
+ * gfx950 GPU.  It follows the proportional-allocation kernel strategy of §3.2
+ * (exact tile statistics, a global partition function, then a parallel gather
+ * in which each tile draws exactly the samples that fall into its share of the
+ * probability mass).
+ *
+ * Sampling conventions (the pages leave these open):
+ *   - uniforms: U = (w0 >> 11) * 2^-53, w0 = word 0 of Philox4x64-10 (Salmon
+ *     et al., SC 2011) with key (seed, 0) and counter (j, h, b, 0) for draw j
+ *     of query head h of sequence b;
+ *   - targets: multinomial sorts U_0..U_{S-1}; stratified t_m = (m + U_m) / S;
+ *     systematic t_m = (m + U_0) / S;
+ *   - key i is chosen for target t iff F(i) <= t < F(i+1), F the CDF of p
+ *     (Appendix A.4); a target at or past F(n) takes the last key of positive
+ *     mass;
+ *   - idx lists the S chosen logical token positions in ascending target
+ *     order; a sequence of length 0 gives o = 0 and idx = -1.
+ *
+ * Ownership and execution: the caller allocates and owns every buffer (all
+ * device pointers below point to device memory on the current HIP device).
+ * The library never allocates device memory, never synchronises, and keeps no
+ * state between calls; every kernel is enqueued on the given stream (NULL:
+ * the default stream), so calls can be captured into a HIP graph.  Host-side
+ * argument checks happen before anything is enqueued; on any non-OK status
+ * nothing was enqueued except where santa_last_error() says otherwise.
+ * Errors raised while kernels run surface at the caller's next
+ * synchronisation.  Two calls that share a workspace must not overlap.
+ */
+#ifndef SANTA_H
+#define SANTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SANTA_ABI_VERSION 1
+
+typedef enum santa_status {
+    SANTA_STATUS_OK = 0,
+    SANTA_STATUS_INVALID_ARGUMENT = 1,     /* null pointer, bad size, misaligned buffer */
+    SANTA_STATUS_UNSUPPORTED = 2,          /* valid but not built: head_dim, group size, S range */
+    SANTA_STATUS_WORKSPACE_TOO_SMALL = 3,
+    SANTA_STATUS_HIP_ERROR = 4             /* a HIP launch failed; see santa_last_error() */
+} santa_status;
+
+/* Sampling rules (§2 and §2.1). */
+enum {
+    SANTA_MODE_MULTINOMIAL = 0,   /* S i.i.d. draws from p (SANTA) */
+    SANTA_MODE_STRATIFIED = 1,    /* one independent draw per stratum [m/S, (m+1)/S) (S2ANTA-strat) */
+    SANTA_MODE_SYSTEMATIC = 2     /* one offset shared by all strata (S2ANTA-sys) */
+};
+
+/* Element type of q, K and V. */
+enum {
+    SANTA_DTYPE_BF16 = 0,
+    SANTA_DTYPE_F32 = 1
+};
+
+/*
+ * Problem shape and KV-cache layout.
+ *
+ * q is [batch, num_q_heads, head_dim], dense.  Query head h reads KV head
+ * h / G.  Row (token i, KV head g) of a cache lives at element offset
+ *   contiguous (page_size == 0):  b * kv_stride_seq + i * kv_stride_tok + g * kv_stride_head
+ *   paged      (page_size  > 0):  P * kv_stride_seq + (i % page_size) * kv_stride_tok
+ *                                 + g * kv_stride_head,
+ *                                 P = block_table[b * pages_per_seq + i / page_size]
+ * and holds head_dim contiguous elements.  K and V share the layout.  Every
+ * row must start on a 16-byte boundary.
+ */
+typedef struct santa_shape {
+    int32_t batch;            /* B >= 1 */
+    int32_t num_q_heads;      /* Hq >= 1 */
+    int32_t num_kv_heads;     /* Hkv >= 1, Hq % Hkv == 0, G = Hq / Hkv in {1, 2, 4, 7, 8} */
+    int32_t head_dim;         /* d in {64, 128} */
+    int32_t max_seq_len;      /* n_max >= 1; seq_lens are clamped to [0, n_max] on the device */
+    int32_t page_size;        /* 0: contiguous cache; else a power of two >= 16 */
+    int32_t pages_per_seq;    /* paged: row length of block_table, >= ceil(n_max / page_size) */
+    int32_t num_pages;        /* paged: pages in each cache; table entries are clamped to [0, num_pages) */
+    int32_t dtype;            /* SANTA_DTYPE_* of q, K and V */
+    int32_t split_size;       /* keys per split of the score pass: 0 (library default) or a
+                                 multiple of 64 in [64, 1024] */
+    int64_t kv_stride_seq;    /* elements between sequences (contiguous) or pages (paged) */
+    int64_t kv_stride_tok;    /* elements between consecutive tokens */
+    int64_t kv_stride_head;   /* elements between KV heads */
+} santa_shape;
+
+/*
+ * Workspace layout (byte offsets into the caller's workspace, 256-byte aligned):
+ *   scores  fp32 [B, Hq, num_splits * split_size]  scaled scores s_i of every key
+ *           (the "score stash" of §3.2, Pass 1), row b*Hq+h starts at
+ *           scores_offset + (b*Hq+h) * score_row_bytes;
+ *   stats   [B, Hq, num_splits] records {float m; float pad; double l}: per split
+ *           the maximum score m and l = sum exp(s_i - m) (the tile partition
+ *           functions of §3.2, Pass 1);
+ *   targets fp64 [B, Hq, S]: sorted multinomial targets (mode 0 only, else empty).
+ * Entries of splits at or past a sequence's length are left unwritten.
+ */
+typedef struct santa_workspace_layout {
+    size_t total_bytes;
+    size_t scores_offset;
+    size_t score_row_bytes;
+    size_t stats_offset;
+    size_t targets_offset;
+    int32_t split_size;
+    int32_t num_splits;       /* ceil(n_max / split_size) */
+} santa_workspace_layout;
+
+/* Version of this ABI (SANTA_ABI_VERSION of the built library). */
+int32_t santa_abi_version(void);
+
+/* Human-readable name of a status code; never NULL. */
+const char* santa_status_string(santa_status status);
+
+/* Detail of the last non-OK status returned on this host thread ("" if none). */
+const char* santa_last_error(void);
+
+/*
+ * Workspace layout for a problem.  Host-only arithmetic: touches no device.
+ * Returns INVALID_ARGUMENT / UNSUPPORTED for shapes santa_decode would reject.
+ */
+santa_status santa_workspace_layout_query(const santa_shape* shape, int32_t num_samples,
+                                          int32_t mode, santa_workspace_layout* out);
+
+/* Bytes of workspace santa_decode needs (the total_bytes of the layout). */
+santa_status santa_workspace_size(const santa_shape* shape, int32_t num_samples, int32_t mode,
+                                  size_t* bytes);
+
+/*
+ * One SANTA decode step.
+ *
+ *   q            [B, Hq, d] dtype, device
+ *   k_cache      K rows, dtype, device, layout as in santa_shape
+ *   v_cache      V rows, same layout
+ *   seq_lens     [B] int32, device: n_b, the number of valid tokens of sequence b
+ *   block_table  [B, pages_per_seq] int32, device; NULL iff page_size == 0
+ *   num_samples  S, 1 <= S <= 65536 (multinomial: S <= 8192); may exceed n_b
+ *   mode         SANTA_MODE_*
+ *   seed         key word 0 of the Philox generator
+ *   o            [B, Hq, d] fp32, device, output: the SANTA estimate (Eq. 3)
+ *   idx          [B, Hq, S] int32, device, output: sampled token positions
+ *   workspace    device scratch of at least santa_workspace_size() bytes,
+ *                256-byte aligned; its contents need no initialisation
+ *   stream       hipStream_t to enqueue on (NULL: default stream)
+ *
+ * The result is a deterministic function of the inputs and seed except for
+ * the order of the fp32 additions that form o.
+ */
+santa_status santa_decode(const santa_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* seq_lens,
+                          const int32_t* block_table, int32_t num_samples, int32_t mode,
+                          uint64_t seed, float* o, int32_t* idx, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of santa_decode, for per-stage checks and timing.  Calling
+ * santa_score_pass then santa_sample_pass on one stream with the same
+ * arguments is exactly santa_decode.
+ *
+ * santa_score_pass: the score pass of §3.2, Pass 1 -- fills the workspace's
+ *   scores and stats (and, for multinomial sampling, the sorted targets), and
+ *   zeroes o.  Reads q, K, seq_lens, block_table.
+ * santa_sample_pass: global partition function, budget allocation and
+ *   parallel gather (§3.2 steps 2-3) -- writes idx and accumulates o.  Reads
+ *   the workspace written by santa_score_pass, V, seq_lens, block_table.
+ */
+santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens,
+                              const int32_t* block_table, int32_t num_samples, int32_t mode,
+                              uint64_t seed, float* o, int32_t* idx, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+santa_status santa_sample_pass(const santa_shape* shape, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* seq_lens,
+                               const int32_t* block_table, int32_t num_samples, int32_t mode,
+                               uint64_t seed, float* o, int32_t* idx, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANTA_H */

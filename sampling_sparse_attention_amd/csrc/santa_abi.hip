@@ -1,0 +1,270 @@
+// C ABI of libsanta: host-side validation, workspace layout and kernel dispatch.
+// Every check runs on the host before anything is enqueued; the library keeps
+// no state between calls apart from a per-thread error message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "santa.h"
+#include "santa_internal.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+santa_status fail(santa_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof(g_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int default_split(const santa_shape& s, int G) {
+    // Enough workgroups to cover the 256 compute units several times over,
+    // but few splits per head: every sample-pass workgroup reads the
+    // statistics of all splits of its heads.
+    const int64_t units = (int64_t)s.batch * s.num_kv_heads;
+    int split = 512;
+    while (split > 128 && units * ((s.max_seq_len + split - 1) / split) < 1024) split >>= 1;
+    while (santa::sample_lds_bytes(G, s.head_dim, split) > 65536 && split > 64) split >>= 1;
+    return split;
+}
+
+struct Plan {
+    int G, split, T, elem_bytes;
+    santa_workspace_layout layout;
+};
+
+santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan) {
+    if (!s) return fail(SANTA_STATUS_INVALID_ARGUMENT, "shape is NULL");
+    if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "batch, num_q_heads and num_kv_heads must be >= 1");
+    if (s->num_q_heads % s->num_kv_heads)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    s->num_q_heads, s->num_kv_heads);
+    const int G = s->num_q_heads / s->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 7 && G != 8)
+        return fail(SANTA_STATUS_UNSUPPORTED, "group size %d not built (1, 2, 4, 7, 8)", G);
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return fail(SANTA_STATUS_UNSUPPORTED, "head_dim %d not built (64, 128)", s->head_dim);
+    if (s->dtype != SANTA_DTYPE_BF16 && s->dtype != SANTA_DTYPE_F32)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "unknown dtype %d", s->dtype);
+    if (s->max_seq_len < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "max_seq_len must be >= 1");
+    const int eb = s->dtype == SANTA_DTYPE_BF16 ? 2 : 4;
+    if (s->page_size != 0) {
+        if (s->page_size < 16 || !is_pow2(s->page_size) || s->page_size > (1 << 20))
+            return fail(SANTA_STATUS_INVALID_ARGUMENT, "page_size %d is not a power of two in [16, 2^20]",
+                        s->page_size);
+        const int64_t need = ((int64_t)s->max_seq_len + s->page_size - 1) / s->page_size;
+        if (s->pages_per_seq < need)
+            return fail(SANTA_STATUS_INVALID_ARGUMENT, "pages_per_seq %d < ceil(max_seq_len / page_size) = %lld",
+                        s->pages_per_seq, (long long)need);
+        if (s->num_pages < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "num_pages must be >= 1");
+    }
+    if (s->kv_stride_tok < 1 || s->kv_stride_seq < 0 || s->kv_stride_head < 0)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "KV strides must be non-negative (token stride >= 1)");
+    if ((s->kv_stride_tok * eb) % 16 || (s->kv_stride_seq * eb) % 16 || (s->kv_stride_head * eb) % 16)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "KV strides must keep every row 16-byte aligned");
+    if (mode < SANTA_MODE_MULTINOMIAL || mode > SANTA_MODE_SYSTEMATIC)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "unknown sampling mode %d", mode);
+    if (S < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "num_samples must be >= 1 (got %d)", S);
+    if (S > santa::kMaxSamples)
+        return fail(SANTA_STATUS_UNSUPPORTED, "num_samples %d above %d", S, santa::kMaxSamples);
+    if (mode == SANTA_MODE_MULTINOMIAL && S > santa::kMaxSortSamples)
+        return fail(SANTA_STATUS_UNSUPPORTED, "multinomial sampling supports num_samples <= %d",
+                    santa::kMaxSortSamples);
+    int split = s->split_size;
+    if (split == 0) {
+        split = default_split(*s, G);
+    } else if (split < 64 || split > santa::kMaxSplit || split % 64) {
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "split_size %d is not a multiple of 64 in [64, %d]",
+                    split, santa::kMaxSplit);
+    }
+    if (santa::sample_lds_bytes(G, s->head_dim, split) > 65536 ||
+        santa::score_lds_bytes(G, split) > 65536)
+        return fail(SANTA_STATUS_UNSUPPORTED, "split_size %d needs more than 64 KiB of LDS for group %d",
+                    split, G);
+    const int64_t T = ((int64_t)s->max_seq_len + split - 1) / split;
+    if ((int64_t)s->batch * s->num_kv_heads * T >= (1ll << 31) || (int64_t)s->batch * s->num_q_heads >= (1ll << 31))
+        return fail(SANTA_STATUS_UNSUPPORTED, "problem too large for one launch");
+
+    plan->G = G;
+    plan->split = split;
+    plan->T = (int)T;
+    plan->elem_bytes = eb;
+    santa_workspace_layout& L = plan->layout;
+    const size_t rows = (size_t)s->batch * s->num_q_heads;
+    L.split_size = split;
+    L.num_splits = (int32_t)T;
+    L.score_row_bytes = (size_t)T * split * sizeof(float);
+    L.scores_offset = 0;
+    L.stats_offset = align256(L.scores_offset + rows * L.score_row_bytes);
+    L.targets_offset = align256(L.stats_offset + rows * (size_t)T * sizeof(santa::SplitStat));
+    const size_t targets = mode == SANTA_MODE_MULTINOMIAL ? rows * (size_t)S * sizeof(double) : 0;
+    L.total_bytes = align256(L.targets_offset + targets);
+    return SANTA_STATUS_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+santa_status make_params(const santa_shape* s, const void* q, const void* k, const void* v,
+                         const int32_t* seq_lens, const int32_t* block_table, int32_t S, int32_t mode,
+                         uint64_t seed, float* o, int32_t* idx, void* ws, size_t ws_bytes,
+                         santa::Params* p, Plan* plan) {
+    santa_status st = make_plan(s, S, mode, plan);
+    if (st != SANTA_STATUS_OK) return st;
+    if (!q || !k || !v || !seq_lens || !o || !idx || !ws)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "a required pointer is NULL");
+    if ((s->page_size != 0) != (block_table != nullptr))
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "block_table must be given exactly when page_size > 0");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "q, k_cache and v_cache must be 16-byte aligned");
+    if (!aligned(o, 16) || !aligned(idx, 4) || !aligned(seq_lens, 4) ||
+        (block_table && !aligned(block_table, 4)))
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "o must be 16-byte and idx/seq_lens/block_table 4-byte aligned");
+    if (!aligned(ws, 256)) return fail(SANTA_STATUS_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (ws_bytes < plan->layout.total_bytes)
+        return fail(SANTA_STATUS_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes,
+                    plan->layout.total_bytes);
+
+    const santa_workspace_layout& L = plan->layout;
+    char* w = static_cast<char*>(ws);
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->seq_lens = seq_lens;
+    p->block_table = block_table;
+    p->o = o;
+    p->idx = idx;
+    p->scores = reinterpret_cast<float*>(w + L.scores_offset);
+    p->stats = reinterpret_cast<santa::SplitStat*>(w + L.stats_offset);
+    p->targets = reinterpret_cast<double*>(w + L.targets_offset);
+    p->stride_seq = s->kv_stride_seq;
+    p->stride_tok = s->kv_stride_tok;
+    p->stride_head = s->kv_stride_head;
+    p->score_row = (int64_t)plan->T * plan->split;
+    p->seed = seed;
+    p->scale = (float)(1.0 / __builtin_sqrt((double)s->head_dim));
+    p->B = s->batch;
+    p->Hq = s->num_q_heads;
+    p->Hkv = s->num_kv_heads;
+    p->G = plan->G;
+    p->D = s->head_dim;
+    p->n_max = s->max_seq_len;
+    p->page_shift = -1;
+    if (s->page_size) {
+        int sh = 0;
+        while ((1 << sh) < s->page_size) ++sh;
+        p->page_shift = sh;
+    }
+    p->pages_per_seq = s->pages_per_seq;
+    p->num_pages = s->num_pages;
+    p->split = plan->split;
+    p->T = plan->T;
+    p->S = S;
+    p->mode = mode;
+    return SANTA_STATUS_OK;
+}
+
+santa_status hip_check(hipError_t e, const char* what) {
+    if (e == hipSuccess) return SANTA_STATUS_OK;
+    return fail(SANTA_STATUS_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+enum Stage { kScore = 1, kSample = 2 };
+
+santa_status run(int stages, const santa_shape* s, const void* q, const void* k, const void* v,
+                 const int32_t* seq_lens, const int32_t* block_table, int32_t S, int32_t mode,
+                 uint64_t seed, float* o, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    santa::Params p;
+    Plan plan;
+    santa_status st = make_params(s, q, k, v, seq_lens, block_table, S, mode, seed, o, idx, ws,
+                                  ws_bytes, &p, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (stages & kScore) {
+        if (mode == SANTA_MODE_MULTINOMIAL) {
+            st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
+            if (st != SANTA_STATUS_OK) return st;
+        }
+        st = hip_check(santa::launch_score(p, s->dtype, hs), "launching the score pass");
+        if (st != SANTA_STATUS_OK) return st;
+    }
+    if (stages & kSample) {
+        st = hip_check(santa::launch_sample(p, s->dtype, hs), "launching the sample pass");
+        if (st != SANTA_STATUS_OK) return st;
+    }
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t santa_abi_version(void) { return SANTA_ABI_VERSION; }
+
+const char* santa_status_string(santa_status status) {
+    switch (status) {
+        case SANTA_STATUS_OK: return "ok";
+        case SANTA_STATUS_INVALID_ARGUMENT: return "invalid argument";
+        case SANTA_STATUS_UNSUPPORTED: return "unsupported";
+        case SANTA_STATUS_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SANTA_STATUS_HIP_ERROR: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* santa_last_error(void) { return g_error; }
+
+santa_status santa_workspace_layout_query(const santa_shape* shape, int32_t num_samples, int32_t mode,
+                                          santa_workspace_layout* out) {
+    if (!out) return fail(SANTA_STATUS_INVALID_ARGUMENT, "out is NULL");
+    Plan plan;
+    santa_status st = make_plan(shape, num_samples, mode, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    *out = plan.layout;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_workspace_size(const santa_shape* shape, int32_t num_samples, int32_t mode,
+                                  size_t* bytes) {
+    if (!bytes) return fail(SANTA_STATUS_INVALID_ARGUMENT, "bytes is NULL");
+    Plan plan;
+    santa_status st = make_plan(shape, num_samples, mode, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    *bytes = plan.layout.total_bytes;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_decode(const santa_shape* shape, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                          int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return run(kScore | kSample, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples,
+               mode, seed, o, idx, workspace, workspace_bytes, stream);
+}
+
+santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                              int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return run(kScore, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed,
+               o, idx, workspace, workspace_bytes, stream);
+}
+
+santa_status santa_sample_pass(const santa_shape* shape, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                               int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return run(kSample, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed,
+               o, idx, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+"""The C ABI on the host: libsanta.so loads, exports every symbol include/santa.h
+declares, and validates arguments before touching any device (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sampling_sparse_attention_amd as santa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "santa.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(santa.library_path):
+        from sampling_sparse_attention_amd import build
+        build.build()
+    return santa.library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(santa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert len(declared) == 8
+    out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (santa_\w+)", out))
+    assert set(declared) <= exported
+    assert set(declared) == set(santa.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    version = int(re.search(r"#define SANTA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.santa_abi_version() == version
+    names = [lib.santa_status_string(s).decode() for s in range(5)]
+    assert names == ["ok", "invalid argument", "unsupported", "workspace too small", "HIP error"]
+    assert lib.santa_status_string(99).decode() == "unknown status"
+
+
+def _shape(**kw):
+    d = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_seq_len=32768, page_size=0,
+             pages_per_seq=0, num_pages=0, dtype=0, split_size=0,
+             kv_stride_seq=32768 * 8 * 128, kv_stride_tok=8 * 128, kv_stride_head=128)
+    d.update(kw)
+    return santa.Shape(**d)
+
+
+def _status_of_size(lib, shape, S=256, mode=2):
+    n = ctypes.c_size_t()
+    return lib.santa_workspace_size(ctypes.byref(shape) if shape is not None else None, S, mode,
+                                    ctypes.byref(n)), n.value
+
+
+def test_workspace_layout_llama_shape(lib):
+    lay = santa.santa_workspace_layout_query(_shape(), 256, 2)
+    T, split = lay.num_splits, lay.split_size
+    assert split % 64 == 0 and T * split >= 32768 and (T - 1) * split < 32768
+    assert lay.score_row_bytes == T * split * 4
+    assert lay.stats_offset >= 32 * lay.score_row_bytes
+    assert lay.targets_offset >= lay.stats_offset + 32 * T * 16
+    assert lay.total_bytes >= lay.targets_offset and lay.total_bytes % 256 == 0
+    assert santa.santa_workspace_size(_shape(), 256, 2) == lay.total_bytes
+    # multinomial keeps S sorted targets per head
+    lay0 = santa.santa_workspace_layout_query(_shape(), 256, 0)
+    assert lay0.total_bytes >= lay0.targets_offset + 32 * 256 * 8
+    lay_split = santa.santa_workspace_layout_query(_shape(split_size=128), 256, 2)
+    assert lay_split.split_size == 128 and lay_split.num_splits == 256
+
+
+@pytest.mark.parametrize("kw,S,mode,want", [
+    (dict(num_q_heads=30), 256, 2, INVALID),
+    (dict(num_q_heads=24), 256, 2, UNSUPPORTED),        # G = 3
+    (dict(head_dim=96), 256, 2, UNSUPPORTED),
+    (dict(dtype=7), 256, 2, INVALID),
+    (dict(max_seq_len=0), 256, 2, INVALID),
+    (dict(batch=0), 256, 2, INVALID),
+    (dict(), 0, 2, INVALID),
+    (dict(), 256, 3, INVALID),
+    (dict(), 65536, 2, UNSUPPORTED),
+    (dict(), 8193, 0, UNSUPPORTED),
+    (dict(), 8192, 0, OK),
+    (dict(), 65535, 1, OK),
+    (dict(split_size=100), 256, 2, INVALID),
+    (dict(split_size=2048), 256, 2, INVALID),
+    (dict(page_size=8, pages_per_seq=4096, num_pages=4096), 256, 2, INVALID),
+    (dict(page_size=24, pages_per_seq=4096, num_pages=4096), 256, 2, INVALID),
+    (dict(page_size=16, pages_per_seq=100, num_pages=4096), 256, 2, INVALID),
+    (dict(page_size=16, pages_per_seq=2048, num_pages=0), 256, 2, INVALID),
+    (dict(page_size=16, pages_per_seq=2048, num_pages=2048), 256, 2, OK),
+    (dict(kv_stride_tok=1001), 256, 2, INVALID),         # rows not 16-byte aligned
+    (dict(kv_stride_tok=0), 256, 2, INVALID),
+    (dict(num_q_heads=64, num_kv_heads=8, split_size=1024), 256, 2, UNSUPPORTED),  # LDS
+])
+def test_host_validation(lib, kw, S, mode, want):
+    st, _ = _status_of_size(lib, _shape(**kw), S, mode)
+    assert st == want, lib.santa_last_error().decode()
+    if want != OK:
+        assert lib.santa_last_error().decode() != ""
+
+
+def test_null_shape_is_rejected(lib):
+    st, _ = _status_of_size(lib, None)
+    assert st == INVALID
+
+
+def test_decode_rejects_bad_pointers_before_launch(lib):
+    """Every failing check returns before anything reaches a device (none exists here)."""
+    shape = _shape(max_seq_len=1024, kv_stride_seq=1024 * 8 * 128)
+    need = santa.santa_workspace_size(shape, 64, 2)
+    fake = ctypes.c_void_p(1 << 20)                 # aligned, never dereferenced
+    args = [fake] * 4 + [None]
+    fn = lib.santa_decode
+
+    def call(q=fake, k=fake, v=fake, lens=fake, bt=None, S=64, mode=2, o=fake, idx=fake, ws=fake,
+             ws_bytes=need, shp=shape):
+        return fn(ctypes.byref(shp), q, k, v, lens, bt, S, mode, ctypes.c_uint64(0), o, idx, ws,
+                  ws_bytes, None)
+
+    assert call(q=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(ws=None) == INVALID
+    assert call(bt=fake) == INVALID                 # table given for a contiguous cache
+    assert call(q=ctypes.c_void_p((1 << 20) + 2)) == INVALID
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == INVALID
+    assert call(ws_bytes=need - 1) == WS_SMALL
+    assert "needs" in lib.santa_last_error().decode()
+    paged = _shape(max_seq_len=1024, page_size=16, pages_per_seq=64, num_pages=64)
+    assert call(shp=paged) == INVALID               # paged without a table
+    assert call(S=0) == INVALID
+    for name in ("santa_score_pass", "santa_sample_pass"):
+        f = getattr(lib, name)
+        assert f(ctypes.byref(shape), None, fake, fake, fake, None, 64, 2, ctypes.c_uint64(0),
+                 fake, fake, fake, need, None) == INVALID
+    del args

@@ -128,7 +128,7 @@ def _storage_dtype(w: Workload) -> torch.dtype:
     raise ValueError(f"unknown dtype {w.dtype!r}")
 
 
-def make_inputs(w: Workload, seed: int = 0, device="cpu", chunk_tokens: int = 1 << 22) -> dict:
+def make_inputs(w: Workload, seed: int = 0, device="cpu", chunk_tokens: int = 1 << 18) -> dict:
     """Draw the inputs of workload ``w`` on ``device``.
 
     Returns a dict with ``q``, ``k``, ``v`` (storage dtype), ``seq_lens``
@@ -250,3 +250,16 @@ def dense_read_bytes(w: Workload, seq_lens) -> int:
     """Bytes a dense decode step reads: every K and every V row."""
     row = w.head_dim * w.elem_bytes
     return 2 * int(sum(int(n) for n in seq_lens)) * w.kv_heads * row
+
+
+def unique_v_rows(idx: torch.Tensor, group: int) -> int:
+    """Distinct (sequence, KV head, token) rows among sampled indices ``idx [B, Hq, S]``
+    (negative entries mark empty sequences and are not rows)."""
+    B, Hq, S = idx.shape
+    per_group = idx.reshape(B, Hq // group, group * S)
+    total = 0
+    for b in range(B):
+        for g in range(Hq // group):
+            u = torch.unique(per_group[b, g])
+            total += int((u >= 0).sum())
+    return total
