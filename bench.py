@@ -67,7 +67,28 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch every call from Python, no HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run plain device-to-device copies of BYTES bytes (the reference kernel "
+                         "for scaling HBM byte counters) and print their bandwidth")
     return ap.parse_args()
+
+
+def calibrate_copy(nbytes: int, reps: int = 10):
+    """Plain copies of a known size: what FETCH_SIZE / WRITE_SIZE read for them
+    converts the counters of the SANTA kernels into bytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    t = start.elapsed_time(end) / reps * 1e-3
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps, "copy_us": t * 1e6,
+                      "read_plus_write_gbs": 2 * nbytes / t / 1e9}))
 
 
 def make_copies(w, n, device):
@@ -195,6 +216,9 @@ def main():
     santa.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     w = W.WORKLOADS[args.workload]
     S = args.samples or w.samples[0]
     mode = w.modes[-1] if args.mode is None else args.mode
