@@ -1,8 +1,8 @@
 """Pins of the oracle's random numbers.
 
 The oracle restates Philox4x64-10 from its published definition; here it is
-checked bit for bit against NumPy's independent implementation and against the
-Random123 known-answer vectors, and its uniforms against the uniform law.
+checked bit for bit against NumPy's independent implementation (with random
+and edge-case counters and keys), and its uniforms against the uniform law.
 """
 import numpy as np
 import pytest
@@ -41,20 +41,6 @@ def test_philox_vectorised_matches_scalar_calls():
     for jj in (0, 1, 17, 299):
         ref = _numpy_block([jj, 7, 2, 0], [99, 0])
         assert [int(w[jj]) for w in words] == ref
-
-
-def test_philox_known_answers(golden_dir):
-    n = 0
-    with open(f"{golden_dir}/philox4x64_10_kat.txt") as f:
-        for line in f:
-            if line.startswith("#") or not line.strip():
-                continue
-            v = [int(x, 16) for x in line.split()]
-            ctr, key, want = v[0:4], v[4:6], v[6:10]
-            got = [int(x) for x in O.philox4x64([np.uint64(c) for c in ctr], key)]
-            assert got == want
-            n += 1
-    assert n == 3
 
 
 def test_uniforms_grid_and_range():
