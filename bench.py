@@ -1,15 +1,18 @@
 """Benchmark of one SANTA decode step on one MI355X.
 
-A step is one ``santa_decode`` call (score pass + sample pass) over one batch
-of synthetic input.  The default workload is the Llama-3.1-8B-shaped layer:
+A step is one ``santa_decode`` call over one batch of synthetic input: the
+fused kernel (scores, global partition function, sampling and gather in one
+launch), plus the target sort for multinomial sampling.  The default workload is the Llama-3.1-8B-shaped layer:
 batch 1, 32 query / 8 KV heads, d = 128, 32768 bf16 keys, S = 256 systematic
 samples.  ``--kv-copies`` independent caches (default 8, 1 GiB) are cycled
 through, one per step like the layers of a model, so that K is read from HBM
 and not from the 256 MB Infinity Cache.
 
 Prints one JSON line: throughput in heads x batch per second, the roofline of
-the dominant kernel (the score pass, bound by HBM bandwidth) and the CPU oracle
-timed on a bounded sample of the same workload.
+the dominant kernel (the fused decode kernel, bound by HBM bandwidth: all of K
+plus the distinct sampled V rows per launch), the two-kernel path's stage
+times for comparison, and the CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -30,7 +33,7 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "decode attention steps/sec (heads×batch) at 32k ctx; achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ["santa_score.hip", "santa_device.h", "santa_internal.h"]
+KERNEL_SOURCES = ["santa_fused.hip", "santa_split.h", "santa_device.h", "santa_internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -42,9 +45,9 @@ def kernel_source_hash() -> str:
 
 
 def counter_traffic(workload: str):
-    """HBM bytes per score-pass launch from the committed rocprofv3 counter
+    """HBM bytes per fused-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"score_pass_{workload}_counters.json")
+    path = os.path.join(ROOT, "profiles", f"fused_kernel_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -235,8 +238,8 @@ def main():
     torch.cuda.synchronize()
     print("[bench] timing steps", file=sys.stderr, flush=True)
     t_step = timed(run.step, args.steps, args.eager, ncopies)
-    t_score = timed(run.score, args.steps, args.eager, ncopies)
-    t_sample = timed(run.sample, args.steps, args.eager, ncopies)
+    # the two-kernel path (score pass + sample pass), for comparison
+    t_two = timed(lambda c: (run.score(c), run.sample(c)), args.steps, args.eager, ncopies)
 
     # algorithmic traffic of one step: all K rows + distinct sampled V rows
     lens = copies[0]["seq_lens"].cpu()
@@ -246,11 +249,11 @@ def main():
         torch.cuda.synchronize()
         uniq.append(W.unique_v_rows(run.idx.cpu(), w.group))
     uniq_mean = sum(uniq) / len(uniq)
-    k_bytes = int(lens.sum()) * w.kv_heads * w.head_dim * w.elem_bytes
     alg_bytes = W.traffic_bytes(w, lens.tolist(), int(round(uniq_mean)))
     dense = W.dense_read_bytes(w, lens.tolist())
-    achieved = k_bytes / t_score / 1e9
+    achieved = alg_bytes / t_step / 1e9
     traffic = counter_traffic(w.name)
+    path = santa.santa_decode_path(run.shape, S, mode)
 
     rec = {
         "metric": METRIC,
@@ -269,15 +272,15 @@ def main():
                    "head_dim": w.head_dim, "seq_len": w.seq_len, "samples": S,
                    "mode": W.MODE_NAMES[mode], "split_size": lay.split_size,
                    "kv_copies": ncopies, "launch": "eager" if args.eager else "hip_graph"},
-        "roofline": {"bound": "hbm", "kernel": "score pass", "achieved": achieved,
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "bytes_per_launch": k_bytes,
-                     "avg_launch_us": t_score * 1e6},
-        "step": {"score_pass_us": t_score * 1e6, "sample_pass_us": t_sample * 1e6,
-                 "algorithmic_bytes": alg_bytes, "unique_v_rows": uniq_mean,
-                 "hbm_gbs": alg_bytes / t_step / 1e9,
-                 "hbm_frac": alg_bytes / t_step / 1e9 / PEAK_HBM_GBS,
-                 "dense_read_bytes": dense,
+        "roofline": {"bound": "hbm",
+                     "kernel": "fused_kernel" if path == santa.PATH_FUSED else "score+sample",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "bytes_per_launch": alg_bytes, "avg_launch_us": t_step * 1e6},
+        "step": {"decode_us": t_step * 1e6, "decode_path": path,
+                 "two_kernel_step_us": t_two * 1e6,
+                 "algorithmic_bytes": alg_bytes, "k_bytes": int(lens.sum()) * w.kv_heads * w.head_dim * w.elem_bytes,
+                 "unique_v_rows": uniq_mean, "dense_read_bytes": dense,
                  "dense_read_us_at_peak": dense / (PEAK_HBM_GBS * 1e9) * 1e6},
         "cpu_baseline": None,
     }

@@ -33,13 +33,21 @@
  *
  * Ownership and execution: the caller allocates and owns every buffer (all
  * device pointers below point to device memory on the current HIP device).
- * The library never allocates device memory, never synchronises, and keeps no
- * state between calls; every kernel is enqueued on the given stream (NULL:
- * the default stream), so calls can be captured into a HIP graph.  Host-side
- * argument checks happen before anything is enqueued; on any non-OK status
- * nothing was enqueued except where santa_last_error() says otherwise.
- * Errors raised while kernels run surface at the caller's next
- * synchronisation.  Two calls that share a workspace must not overlap.
+ * The library never allocates device memory and never synchronises; every
+ * kernel is enqueued on the given stream (NULL: the default stream), so calls
+ * can be captured into a HIP graph.  Host-side argument checks happen before
+ * anything is enqueued; on any non-OK status nothing was enqueued.  Errors
+ * raised while kernels run surface at the caller's next synchronisation.
+ *
+ * State: the library keeps none between calls on the host.  A workspace must
+ * be all zero before its first call (santa_workspace_init, or any zero fill).
+ * Every completed call leaves it all zero again except for the epoch word at
+ * byte 0 (and the error word at byte 4 after a failed wait), so one workspace
+ * large enough for each of them serves calls of any shapes, modes and sample
+ * counts in any order.  The two-kernel path counts as one call from the start
+ * of santa_score_pass to the end of the santa_sample_pass that follows it.
+ * Calls that share a workspace must not overlap (same stream, or ordered by
+ * events).
  */
 #ifndef SANTA_H
 #define SANTA_H
@@ -51,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SANTA_ABI_VERSION 1
+#define SANTA_ABI_VERSION 2
 
 typedef enum santa_status {
     SANTA_STATUS_OK = 0,
@@ -105,20 +113,37 @@ typedef struct santa_shape {
 
 /*
  * Workspace layout (byte offsets into the caller's workspace, 256-byte aligned):
- *   scores  fp32 [B, Hq, num_splits * split_size]  scaled scores s_i of every key
- *           (the "score stash" of §3.2, Pass 1), row b*Hq+h starts at
- *           scores_offset + (b*Hq+h) * score_row_bytes;
- *   stats   [B, Hq, num_splits] records {float m; float pad; double l}: per split
- *           the maximum score m and l = sum exp(s_i - m) (the tile partition
- *           functions of §3.2, Pass 1);
- *   targets fp64 [B, Hq, S]: sorted multinomial targets (mode 0 only, else empty).
- * Entries of splits at or past a sequence's length are left unwritten.
+ *   sync     synchronisation words (barrier_offset bytes at the start): the
+ *            epoch of the last call that published split records (byte 0),
+ *            a 32-bit error word (byte 4) that becomes nonzero if a bounded
+ *            wait of a call gave up (that call's outputs are invalid;
+ *            santa_workspace_init clears it), and per-call arrival counters;
+ *   barrier  [B, Hkv] x 18 lines of 128 bytes: per (sequence, KV head) the
+ *            counts of its splits that have published their records and that
+ *            have added their output in the current call, and 16 copies of a
+ *            flag raised to the call's epoch once all of them published;
+ *   accum    fp32 [B, Hkv, 16, G, d]: partial outputs, added by the splits of a
+ *            (sequence, KV head) into slot (split % 16) and summed into o by
+ *            the last of them;
+ *   records  [B, Hq, num_splits] x 16 bytes: per split the maximum score m and
+ *            l = sum exp(s_i - m) (the tile partition functions of section 3.2,
+ *            Pass 1), each in a 64-bit word tagged with the call's epoch;
+ *   stash    fp32 [B, Hq, num_splits * split_size]: scaled scores s_i (the
+ *            "score stash" of section 3.2, Pass 1), written by
+ *            santa_score_pass and read (and cleared) by santa_sample_pass; row
+ *            b*Hq+h starts at stash_offset + (b*Hq+h) * stash_row_bytes;
+ *   targets  fp64 [B, Hq, S]: sorted multinomial targets (mode 0 only, else
+ *            empty).
+ * All of it except the epoch and error words is zero between calls.
  */
 typedef struct santa_workspace_layout {
     size_t total_bytes;
-    size_t scores_offset;
-    size_t score_row_bytes;
-    size_t stats_offset;
+    size_t sync_offset;
+    size_t barrier_offset;
+    size_t accum_offset;
+    size_t records_offset;
+    size_t stash_offset;
+    size_t stash_row_bytes;
     size_t targets_offset;
     int32_t split_size;
     int32_t num_splits;       /* ceil(n_max / split_size) */
@@ -145,6 +170,21 @@ santa_status santa_workspace_size(const santa_shape* shape, int32_t num_samples,
                                   size_t* bytes);
 
 /*
+ * Zero-fills a workspace (workspace_bytes bytes, 256-byte aligned) with a
+ * kernel on `stream`; required once before the first call on a workspace.
+ */
+santa_status santa_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * How santa_decode will run this problem on the current device: 1 = one fused
+ * kernel (score pass, global budget and gather in one launch), 2 = the score
+ * pass followed by the sample pass.  The fused kernel needs the device to hold
+ * more of its workgroups at once than a sequence has splits.  Returns the
+ * negated santa_status on error.  Queries the HIP runtime, touches no memory.
+ */
+int32_t santa_decode_path(const santa_shape* shape, int32_t num_samples, int32_t mode);
+
+/*
  * One SANTA decode step.
  *
  *   q            [B, Hq, d] dtype, device
@@ -158,7 +198,7 @@ santa_status santa_workspace_size(const santa_shape* shape, int32_t num_samples,
  *   o            [B, Hq, d] fp32, device, output: the SANTA estimate (Eq. 3)
  *   idx          [B, Hq, S] int32, device, output: sampled token positions
  *   workspace    device scratch of at least santa_workspace_size() bytes,
- *                256-byte aligned; its contents need no initialisation
+ *                256-byte aligned, initialised once by santa_workspace_init
  *   stream       hipStream_t to enqueue on (NULL: default stream)
  *
  * The result is a deterministic function of the inputs and seed except for
@@ -175,12 +215,16 @@ santa_status santa_decode(const santa_shape* shape, const void* q, const void* k
  * santa_score_pass then santa_sample_pass on one stream with the same
  * arguments is exactly santa_decode.
  *
- * santa_score_pass: the score pass of §3.2, Pass 1 -- fills the workspace's
- *   scores and stats (and, for multinomial sampling, the sorted targets), and
- *   zeroes o.  Reads q, K, seq_lens, block_table.
+ * santa_score_pass: the score pass of section 3.2, Pass 1 -- fills the
+ *   workspace's stash and records (and, for multinomial sampling, the sorted
+ *   targets), and zeroes o.  Reads q, K, seq_lens, block_table.
  * santa_sample_pass: global partition function, budget allocation and
- *   parallel gather (§3.2 steps 2-3) -- writes idx and accumulates o.  Reads
- *   the workspace written by santa_score_pass, V, seq_lens, block_table.
+ *   parallel gather (section 3.2 steps 2-3) -- writes idx and accumulates o.
+ *   Reads the workspace written by santa_score_pass, V, seq_lens, block_table.
+ *   It must directly follow santa_score_pass with the same arguments on the
+ *   same workspace (it waits, boundedly, for that call's records).
+ * santa_decode runs either these two kernels or one fused kernel with the same
+ * results (santa_decode_path says which).
  */
 santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* seq_lens,

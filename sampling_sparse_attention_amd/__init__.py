@@ -17,8 +17,9 @@ import torch
 __all__ = [
     "MODE_MULTINOMIAL", "MODE_STRATIFIED", "MODE_SYSTEMATIC", "Shape", "WorkspaceLayout",
     "SantaError", "library", "library_path", "make_shape", "santa_workspace_layout_query",
-    "santa_workspace_size", "santa_decode", "santa_score_pass", "santa_sample_pass", "decode",
-    "allocate_workspace", "EXPORTED_SYMBOLS",
+    "santa_workspace_size", "santa_workspace_init", "santa_decode_path", "santa_decode",
+    "santa_score_pass", "santa_sample_pass", "decode", "allocate_workspace", "workspace_error",
+    "EXPORTED_SYMBOLS",
 ]
 
 MODE_MULTINOMIAL = 0
@@ -29,9 +30,11 @@ DTYPE_F32 = 1
 
 EXPORTED_SYMBOLS = (
     "santa_abi_version", "santa_status_string", "santa_last_error",
-    "santa_workspace_layout_query", "santa_workspace_size", "santa_decode",
-    "santa_score_pass", "santa_sample_pass",
+    "santa_workspace_layout_query", "santa_workspace_size", "santa_workspace_init",
+    "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass",
 )
+PATH_FUSED = 1
+PATH_TWO_KERNELS = 2
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG_DIR, "libsanta.so")
@@ -53,10 +56,11 @@ class Shape(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     """Mirror of ``santa_workspace_layout``."""
     _fields_ = [
-        ("total_bytes", ctypes.c_size_t), ("scores_offset", ctypes.c_size_t),
-        ("score_row_bytes", ctypes.c_size_t), ("stats_offset", ctypes.c_size_t),
-        ("targets_offset", ctypes.c_size_t), ("split_size", ctypes.c_int32),
-        ("num_splits", ctypes.c_int32),
+        ("total_bytes", ctypes.c_size_t), ("sync_offset", ctypes.c_size_t),
+        ("barrier_offset", ctypes.c_size_t), ("accum_offset", ctypes.c_size_t),
+        ("records_offset", ctypes.c_size_t), ("stash_offset", ctypes.c_size_t),
+        ("stash_row_bytes", ctypes.c_size_t), ("targets_offset", ctypes.c_size_t),
+        ("split_size", ctypes.c_int32), ("num_splits", ctypes.c_int32),
     ]
 
 
@@ -87,6 +91,10 @@ def library() -> ctypes.CDLL:
                                                      ctypes.POINTER(WorkspaceLayout)]
         lib.santa_workspace_size.restype = ctypes.c_int
         lib.santa_workspace_size.argtypes = [ctypes.POINTER(Shape), i32, i32, ctypes.POINTER(sz)]
+        lib.santa_workspace_init.restype = ctypes.c_int
+        lib.santa_workspace_init.argtypes = [vp, sz, vp]
+        lib.santa_decode_path.restype = i32
+        lib.santa_decode_path.argtypes = [ctypes.POINTER(Shape), i32, i32]
         for name in ("santa_decode", "santa_score_pass", "santa_sample_pass"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
@@ -137,9 +145,32 @@ def santa_workspace_size(shape: Shape, num_samples: int, mode: int) -> int:
     return out.value
 
 
+def santa_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    """Zero-fills a workspace on the device (``santa_workspace_init``)."""
+    _check(library().santa_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          _stream_handle(stream)), "santa_workspace_init")
+
+
+def santa_decode_path(shape: Shape, num_samples: int, mode: int) -> int:
+    """1: ``santa_decode`` runs one fused kernel; 2: the score pass then the sample pass."""
+    r = library().santa_decode_path(ctypes.byref(shape), num_samples, mode)
+    if r < 0:
+        _check(-r, "santa_decode_path")
+    return r
+
+
 def allocate_workspace(shape: Shape, num_samples: int, mode: int, device) -> torch.Tensor:
+    """A workspace of the size the problem needs, initialised by ``santa_workspace_init``."""
     n = santa_workspace_size(shape, num_samples, mode)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    santa_workspace_init(ws)
+    return ws
+
+
+def workspace_error(workspace: torch.Tensor) -> int:
+    """The workspace's error word (nonzero: a bounded wait of a decode call gave up).
+    Reads device memory: synchronises with the current stream."""
+    return int(workspace[4:8].view(torch.int32).item())
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -1,6 +1,7 @@
-// C ABI of libsanta: host-side validation, workspace layout and kernel dispatch.
-// Every check runs on the host before anything is enqueued; the library keeps
-// no state between calls apart from a per-thread error message.
+// C ABI of libsanta: host-side validation, workspace layout, path choice and
+// kernel dispatch.  Every check runs on the host before anything is enqueued;
+// the library keeps no state between calls apart from a per-thread error
+// message.
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -23,14 +24,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
+bool split_fits(int G, int D, int split) {
+    return santa::split_lds_bytes(G, D, split, santa::kThreads) <= santa::kLdsPerWorkgroup;
+}
+
 int default_split(const santa_shape& s, int G) {
-    // Enough workgroups to cover the 256 compute units several times over,
-    // but few splits per head: every sample-pass workgroup reads the
-    // statistics of all splits of its heads.
-    const int64_t units = (int64_t)s.batch * s.num_kv_heads;
-    int split = 512;
-    while (split > 128 && units * ((s.max_seq_len + split - 1) / split) < 1024) split >>= 1;
-    while (santa::sample_lds_bytes(G, s.head_dim, split) > 65536 && split > 64) split >>= 1;
+    int split = 256;
+    while (split < santa::kMaxSplit &&
+           ((int64_t)s.max_seq_len + split - 1) / split > santa::kMaxSplitsPerSeq)
+        split <<= 1;
+    while (split > 64 && !split_fits(G, s.head_dim, split)) split >>= 1;
     return split;
 }
 
@@ -54,6 +57,9 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     if (s->dtype != SANTA_DTYPE_BF16 && s->dtype != SANTA_DTYPE_F32)
         return fail(SANTA_STATUS_INVALID_ARGUMENT, "unknown dtype %d", s->dtype);
     if (s->max_seq_len < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "max_seq_len must be >= 1");
+    if ((int64_t)s->max_seq_len > (int64_t)santa::kMaxSplit * santa::kMaxSplitsPerSeq)
+        return fail(SANTA_STATUS_UNSUPPORTED, "max_seq_len %d above %d", s->max_seq_len,
+                    santa::kMaxSplit * santa::kMaxSplitsPerSeq);
     const int eb = s->dtype == SANTA_DTYPE_BF16 ? 2 : 4;
     if (s->page_size != 0) {
         if (s->page_size < 16 || !is_pow2(s->page_size) || s->page_size > (1 << 20))
@@ -84,11 +90,13 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
         return fail(SANTA_STATUS_INVALID_ARGUMENT, "split_size %d is not a multiple of 64 in [64, %d]",
                     split, santa::kMaxSplit);
     }
-    if (santa::sample_lds_bytes(G, s->head_dim, split) > 65536 ||
-        santa::score_lds_bytes(G, split) > 65536)
-        return fail(SANTA_STATUS_UNSUPPORTED, "split_size %d needs more than 64 KiB of LDS for group %d",
-                    split, G);
+    if (!split_fits(G, s->head_dim, split))
+        return fail(SANTA_STATUS_UNSUPPORTED, "split_size %d needs more than %zu bytes of LDS for group %d",
+                    split, santa::kLdsPerWorkgroup, G);
     const int64_t T = ((int64_t)s->max_seq_len + split - 1) / split;
+    if (T > santa::kMaxSplitsPerSeq)
+        return fail(SANTA_STATUS_UNSUPPORTED, "split_size %d gives %lld splits per sequence (at most %d)",
+                    split, (long long)T, santa::kMaxSplitsPerSeq);
     if ((int64_t)s->batch * s->num_kv_heads * T >= (1ll << 31) || (int64_t)s->batch * s->num_q_heads >= (1ll << 31))
         return fail(SANTA_STATUS_UNSUPPORTED, "problem too large for one launch");
 
@@ -100,10 +108,14 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     const size_t rows = (size_t)s->batch * s->num_q_heads;
     L.split_size = split;
     L.num_splits = (int32_t)T;
-    L.score_row_bytes = (size_t)T * split * sizeof(float);
-    L.scores_offset = 0;
-    L.stats_offset = align256(L.scores_offset + rows * L.score_row_bytes);
-    L.targets_offset = align256(L.stats_offset + rows * (size_t)T * sizeof(santa::SplitStat));
+    L.sync_offset = 0;
+    L.barrier_offset = align256(santa::kSyncBytes);
+    L.accum_offset = align256(L.barrier_offset + (size_t)s->batch * s->num_kv_heads * santa::kBarrierStride * 4);
+    L.records_offset = align256(L.accum_offset + (size_t)s->batch * s->num_q_heads * santa::kOutSlots *
+                                                     s->head_dim * sizeof(float));
+    L.stash_offset = align256(L.records_offset + rows * (size_t)T * 16);
+    L.stash_row_bytes = (size_t)T * split * sizeof(float);
+    L.targets_offset = align256(L.stash_offset + rows * L.stash_row_bytes);
     const size_t targets = mode == SANTA_MODE_MULTINOMIAL ? rows * (size_t)S * sizeof(double) : 0;
     L.total_bytes = align256(L.targets_offset + targets);
     return SANTA_STATUS_OK;
@@ -140,13 +152,16 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->block_table = block_table;
     p->o = o;
     p->idx = idx;
-    p->scores = reinterpret_cast<float*>(w + L.scores_offset);
-    p->stats = reinterpret_cast<santa::SplitStat*>(w + L.stats_offset);
+    p->sync = reinterpret_cast<santa::SyncWords*>(w + L.sync_offset);
+    p->records = reinterpret_cast<unsigned long long*>(w + L.records_offset);
+    p->barrier = reinterpret_cast<unsigned int*>(w + L.barrier_offset);
+    p->accum = reinterpret_cast<float*>(w + L.accum_offset);
+    p->stash = reinterpret_cast<float*>(w + L.stash_offset);
     p->targets = reinterpret_cast<double*>(w + L.targets_offset);
     p->stride_seq = s->kv_stride_seq;
     p->stride_tok = s->kv_stride_tok;
     p->stride_head = s->kv_stride_head;
-    p->score_row = (int64_t)plan->T * plan->split;
+    p->stash_row = (int64_t)plan->T * plan->split;
     p->seed = seed;
     p->scale = (float)(1.0 / __builtin_sqrt((double)s->head_dim));
     p->B = s->batch;
@@ -165,6 +180,7 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->num_pages = s->num_pages;
     p->split = plan->split;
     p->T = plan->T;
+    p->items = (int32_t)((int64_t)s->batch * s->num_kv_heads * plan->T);
     p->S = S;
     p->mode = mode;
     return SANTA_STATUS_OK;
@@ -175,7 +191,19 @@ santa_status hip_check(hipError_t e, const char* what) {
     return fail(SANTA_STATUS_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
 
-enum Stage { kScore = 1, kSample = 2 };
+// How santa_decode runs a problem: 1 = the fused kernel, 2 = score pass +
+// sample pass, 0 = unknown (HIP error).  The fused kernel's workgroups wait for
+// one another, so it runs only when the device holds all of them at once.
+int choose_path(const santa::Params& p, int dtype) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const int per_cu = santa::fused_blocks_per_cu(p, dtype);
+    if (per_cu <= 0) return 0;
+    return (int64_t)per_cu * cus >= (int64_t)p.items ? 1 : 2;
+}
+
+enum Stage { kScore = 1, kSample = 2, kDecode = 3 };
 
 santa_status run(int stages, const santa_shape* s, const void* q, const void* k, const void* v,
                  const int32_t* seq_lens, const int32_t* block_table, int32_t S, int32_t mode,
@@ -186,17 +214,27 @@ santa_status run(int stages, const santa_shape* s, const void* q, const void* k,
                                   ws_bytes, &p, &plan);
     if (st != SANTA_STATUS_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (stages & kScore) {
-        if (mode == SANTA_MODE_MULTINOMIAL) {
-            st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
-            if (st != SANTA_STATUS_OK) return st;
-        }
-        st = hip_check(santa::launch_score(p, s->dtype, hs), "launching the score pass");
+    int path = 2;
+    if (stages == kDecode) {
+        path = choose_path(p, s->dtype);
+        if (path == 0) return fail(SANTA_STATUS_HIP_ERROR, "querying the device for the launch plan failed");
+    }
+    if ((stages & kScore) && mode == SANTA_MODE_MULTINOMIAL) {
+        st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
         if (st != SANTA_STATUS_OK) return st;
     }
-    if (stages & kSample) {
-        st = hip_check(santa::launch_sample(p, s->dtype, hs), "launching the sample pass");
+    if (path == 1) {
+        st = hip_check(santa::launch_fused(p, s->dtype, hs), "launching the fused decode kernel");
         if (st != SANTA_STATUS_OK) return st;
+    } else {
+        if (stages & kScore) {
+            st = hip_check(santa::launch_score(p, s->dtype, hs), "launching the score pass");
+            if (st != SANTA_STATUS_OK) return st;
+        }
+        if (stages & kSample) {
+            st = hip_check(santa::launch_sample(p, s->dtype, hs), "launching the sample pass");
+            if (st != SANTA_STATUS_OK) return st;
+        }
     }
     g_error[0] = '\0';
     return SANTA_STATUS_OK;
@@ -243,12 +281,44 @@ santa_status santa_workspace_size(const santa_shape* shape, int32_t num_samples,
     return SANTA_STATUS_OK;
 }
 
+santa_status santa_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return fail(SANTA_STATUS_INVALID_ARGUMENT, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(SANTA_STATUS_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (workspace_bytes < santa::kSyncBytes)
+        return fail(SANTA_STATUS_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs at least %zu",
+                    workspace_bytes, santa::kSyncBytes);
+    santa_status st = hip_check(santa::launch_clear(workspace, workspace_bytes, static_cast<hipStream_t>(stream)),
+                                "launching the workspace clear");
+    if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+int32_t santa_decode_path(const santa_shape* shape, int32_t num_samples, int32_t mode) {
+    santa::Params p;
+    Plan plan;
+    santa_status st = make_plan(shape, num_samples, mode, &plan);
+    if (st != SANTA_STATUS_OK) return -(int32_t)st;
+    p.G = plan.G;
+    p.D = shape->head_dim;
+    p.split = plan.split;
+    p.T = plan.T;
+    p.items = (int32_t)((int64_t)shape->batch * shape->num_kv_heads * plan.T);
+    const int path = choose_path(p, shape->dtype);
+    if (path == 0) {
+        fail(SANTA_STATUS_HIP_ERROR, "querying the device for the launch plan failed");
+        return -(int32_t)SANTA_STATUS_HIP_ERROR;
+    }
+    g_error[0] = '\0';
+    return path;
+}
+
 santa_status santa_decode(const santa_shape* shape, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
                           int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
                           void* workspace, size_t workspace_bytes, void* stream) {
-    return run(kScore | kSample, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples,
-               mode, seed, o, idx, workspace, workspace_bytes, stream);
+    return run(kDecode, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o,
+               idx, workspace, workspace_bytes, stream);
 }
 
 santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,

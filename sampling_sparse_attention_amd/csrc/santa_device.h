@@ -46,31 +46,122 @@ __device__ __forceinline__ double uniform01(uint64_t seed, int b, int h, uint64_
 }
 
 // ---------------------------------------------------------------------------
-// Cross-lane exchange inside a row of LPR lanes (LPR <= 32).  partner<K>(v)
+// Cross-lane data movement with DPP (VALU-only, no LDS traffic).
+//
+// dpp<CTRL, ROWS>(identity, v): v taken from the lane CTRL names, or
+// `identity` where that lane does not exist or the row is masked off.
+// Controls used (GFX9 DPP): row_shr:n = 0x110+n (lane i of a 16-lane row reads
+// lane i-n of the same row), row_bcast:15 = 0x142 (every lane of row r reads
+// lane 15 of row r-1), row_bcast:31 = 0x143 (rows 2 and 3 read lane 31),
+// row_ror:8 = 0x128, row_half_mirror = 0x141, quad_perm = 0x00..0xFF.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t identity, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_f32(float identity, float v) {
+    return __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(identity), __float_as_uint(v)));
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {   // identity 0
+    const uint32_t lo = dpp_u32<CTRL, ROWS>(0u, (uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, ROWS>(0u, (uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {       // identity +0.0
+    return __longlong_as_double((long long)dpp_u64<CTRL, ROWS>((uint64_t)__double_as_longlong(v)));
+}
+
+// Inclusive scans over the 64 lanes of a wave (Hillis-Steele inside 16-lane
+// rows, then the two row broadcasts).  Every lane of the wave must be active.
+// The order of operations is fixed, so identical inputs give identical bits in
+// every workgroup.
+__device__ __forceinline__ uint64_t wave_scan_add_u64(uint64_t x) {
+    x += dpp_u64<0x111>(x);
+    x += dpp_u64<0x112>(x);
+    x += dpp_u64<0x114>(x);
+    x += dpp_u64<0x118>(x);
+    x += dpp_u64<0x142, 0xA>(x);
+    x += dpp_u64<0x143, 0xC>(x);
+    return x;
+}
+
+__device__ __forceinline__ double wave_scan_add_f64(double x) {
+    x += dpp_f64<0x111>(x);
+    x += dpp_f64<0x112>(x);
+    x += dpp_f64<0x114>(x);
+    x += dpp_f64<0x118>(x);
+    x += dpp_f64<0x142, 0xA>(x);
+    x += dpp_f64<0x143, 0xC>(x);
+    return x;
+}
+
+__device__ __forceinline__ float wave_scan_max_f32(float x) {
+    const float lo = -INFINITY;
+    x = fmaxf(x, dpp_f32<0x111>(lo, x));
+    x = fmaxf(x, dpp_f32<0x112>(lo, x));
+    x = fmaxf(x, dpp_f32<0x114>(lo, x));
+    x = fmaxf(x, dpp_f32<0x118>(lo, x));
+    x = fmaxf(x, dpp_f32<0x142, 0xA>(lo, x));
+    x = fmaxf(x, dpp_f32<0x143, 0xC>(lo, x));
+    return x;
+}
+
+__device__ __forceinline__ int wave_scan_max_i32(int x) {
+    const uint32_t lo = 0x80000000u;
+    x = max(x, (int)dpp_u32<0x111>(lo, (uint32_t)x));
+    x = max(x, (int)dpp_u32<0x112>(lo, (uint32_t)x));
+    x = max(x, (int)dpp_u32<0x114>(lo, (uint32_t)x));
+    x = max(x, (int)dpp_u32<0x118>(lo, (uint32_t)x));
+    x = max(x, (int)dpp_u32<0x142, 0xA>(lo, (uint32_t)x));
+    x = max(x, (int)dpp_u32<0x143, 0xC>(lo, (uint32_t)x));
+    return x;
+}
+
+// The value of lane `src` (uniform) in every lane.
+__device__ __forceinline__ float lane_f32(float v, int src) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ int lane_i32(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int src) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double lane_f64(double v, int src) {
+    return __longlong_as_double((long long)lane_u64((uint64_t)__double_as_longlong(v), src));
+}
+
+// Whole-wave reductions: the result in every lane.
+__device__ __forceinline__ float wave_max_f32(float v) { return lane_f32(wave_scan_max_f32(v), 63); }
+__device__ __forceinline__ int wave_max_i32(int v) { return lane_i32(wave_scan_max_i32(v), 63); }
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) { return lane_u64(wave_scan_add_u64(v), 63); }
+
+// ---------------------------------------------------------------------------
+// Reduce-scatter across the LPR lanes of a K row (LPR <= 32).  partner<K>(v)
 // returns v from a lane that differs from this one in bit K of the lane index
 // and agrees in all higher bits (within the row); lower bits may differ, which
 // a reduce-scatter butterfly (highest bit first) does not care about.
-// Distances below 16 use DPP row operations (no LDS traffic).
 // ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 template <int K>
 __device__ __forceinline__ float partner(float v) {
     if constexpr (K == 16) {
         // ds_swizzle bitmask mode: and 0x1F, or 0, xor 0x10 -> lane ^ 16 within 32
         return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
     } else if constexpr (K == 8) {
-        return dpp_f32<0x128>(v);       // row_ror:8   -> lane ^ 8 within 16
+        return dpp_f32<0x128>(0.0f, v);       // row_ror:8   -> lane ^ 8 within 16
     } else if constexpr (K == 4) {
-        return dpp_f32<0x141>(v);       // row_half_mirror: i <-> 7 - i within 8
+        return dpp_f32<0x141>(0.0f, v);       // row_half_mirror: i <-> 7 - i within 8
     } else if constexpr (K == 2) {
-        return dpp_f32<0x4E>(v);        // quad_perm(2,3,0,1)
+        return dpp_f32<0x4E>(0.0f, v);        // quad_perm(2,3,0,1)
     } else {
         static_assert(K == 1, "distance");
-        return dpp_f32<0xB1>(v);        // quad_perm(1,0,3,2)
+        return dpp_f32<0xB1>(0.0f, v);        // quad_perm(1,0,3,2)
     }
 }
 
@@ -86,9 +177,9 @@ __device__ __forceinline__ void bfly_step(float* a, bool upper) {
     }
 }
 
-// Reduce-scatter of NVP partial sums across the LPR lanes of a row: afterwards
-// lane li of the row holds the complete sums of values [li*NVP/LPR, (li+1)*NVP/LPR)
-// in a[0 .. NVP/LPR).  Requires NVP % LPR == 0 and every lane of the wave active.
+// Afterwards lane li of the row holds the complete sums of values
+// [li*NVP/LPR, (li+1)*NVP/LPR) in a[0 .. NVP/LPR).  Requires NVP % LPR == 0
+// and every lane of the wave active.
 template <int LPR, int NVP>
 __device__ __forceinline__ void row_reduce_scatter(float* a, int li) {
     if constexpr (LPR >= 2) {
@@ -98,46 +189,6 @@ __device__ __forceinline__ void row_reduce_scatter(float* a, int li) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Wave-wide reductions and scans (fixed order, so every workgroup that runs
-// them on the same data gets the same bits).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-__device__ __forceinline__ double wave_inclusive_scan_f64(double v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double y = __shfl_up(v, off, 64);
-        if (lane >= off) v += y;
-    }
-    return v;
-}
-
-__device__ __forceinline__ int wave_inclusive_scan_i32(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(v, off, 64);
-        if (lane >= off) v += y;
-    }
-    return v;
-}
-
 // Orders LDS writes of this wave before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -145,23 +196,19 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The exponential used for every probability mass, in both kernels: the two
-// passes must evaluate exp(s - m) identically for the tile sums of one pass to
-// equal the prefix sums of the other.
-__device__ __forceinline__ float mass_exp(float x) { return expf(x); }
+// The exponential used for every probability mass: the hardware base-2
+// exponential of x * log2(e).  Each mass is evaluated once (the statistics and
+// the in-split CDF share the fixed-point values), and a split's scale factor
+// exp(m_t - M) is evaluated with the same function wherever it is used.  Its
+// relative error (a few 1e-7 for |x| <= 20) is below that of the fp32 scores.
+__device__ __forceinline__ float mass_exp(float x) { return __expf(x); }
 
 // Masses inside a split are summed as 52-bit fixed point (e <= 1, so a split
 // of <= 1024 keys stays below 2^62): integer sums are exact and independent of
-// their order, so the score pass's tile sum l and the sample pass's prefix
-// sums P_i agree to the last bit and P is exactly non-decreasing.
+// their order, so the prefix sums P_i are exactly non-decreasing and their
+// last value is the split's total.
 __device__ __forceinline__ uint64_t fixed_mass(float e) { return (uint64_t)(e * 0x1p52f); }
-constexpr double kFixedUnit = 0x1p-52;
-
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ __forceinline__ double fixed_to_double(uint64_t v) { return (double)v * 0x1p-52; }
 
 // ---------------------------------------------------------------------------
 // Element types of q / K / V.
@@ -182,13 +229,16 @@ struct Bf16 {
                                               __builtin_bit_cast(bf16x2_t, q.w), acc, false);
         return acc;
     }
-    // the 8 elements of a 16-byte chunk, widened exactly to fp32
-    __device__ static __forceinline__ void widen16(const uint4& v, float* out) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(w[i] << 16);
-            out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    // EL (1 or 2) consecutive elements of a V row, widened exactly to fp32
+    template <int EL>
+    __device__ static __forceinline__ void load_row_part(const void* p, float* out) {
+        if constexpr (EL == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+            out[0] = __uint_as_float(w << 16);
+            out[1] = __uint_as_float(w & 0xFFFF0000u);
+        } else {
+            const uint16_t w = *reinterpret_cast<const uint16_t*>(p);
+            out[0] = __uint_as_float((uint32_t)w << 16);
         }
     }
 };
@@ -202,11 +252,15 @@ struct F32 {
         acc = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), acc);
         return acc;
     }
-    __device__ static __forceinline__ void widen16(const uint4& v, float* out) {
-        out[0] = __uint_as_float(v.x);
-        out[1] = __uint_as_float(v.y);
-        out[2] = __uint_as_float(v.z);
-        out[3] = __uint_as_float(v.w);
+    template <int EL>
+    __device__ static __forceinline__ void load_row_part(const void* p, float* out) {
+        if constexpr (EL == 2) {
+            const float2 w = *reinterpret_cast<const float2*>(p);
+            out[0] = w.x;
+            out[1] = w.y;
+        } else {
+            out[0] = *reinterpret_cast<const float*>(p);
+        }
     }
 };
 

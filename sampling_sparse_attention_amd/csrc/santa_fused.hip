@@ -1,0 +1,97 @@
+// Fused SANTA decode kernel: the whole step of section 3.2 of "Stochastic
+// Sparse Attention for Memory-Bound Inference" (score pass, global budget,
+// parallel gather) in one launch, one workgroup per work item -- (sequence,
+// KV head, split) -- with each split's scores kept in LDS across the global
+// step.
+//
+// The only wait is for the statistics of the other splits of the same
+// sequence.  The host launches this kernel only when the device holds every
+// workgroup of the grid at once, so every statistic a workgroup waits for is
+// computed by a running workgroup.
+#include "santa_split.h"
+
+namespace santa {
+
+template <int G, int D, typename E, int NT>
+__device__ __forceinline__ void fused_item(const Params& p, const Item& it, uint32_t epoch,
+                                           unsigned char* smem) {
+    if (it.n == 0) {
+        if (it.t == 0) write_empty<G, D, NT>(p, it);
+        return;
+    }
+    if (it.ns == 0) return;
+    const LdsLayout L = lds_layout(G, D, p.split, NT);
+    float* sc = reinterpret_cast<float*>(smem + L.scratch);
+    int* pages = reinterpret_cast<int*>(smem + L.pages);
+    HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
+
+    load_pages<NT>(p, it, pages);
+    __syncthreads();
+    stream_scores<G, D, E, NT>(p, it, sc, pages);
+    __syncthreads();
+    split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
+    __syncthreads();
+    // a reader re-reads a record until its epoch matches, so the barrier need
+    // not wait for these stores to complete
+    publish_stats<G>(p, it, hs, epoch);
+    group_barrier(p, it, epoch, [&] { systematic_offsets<G, 1>(p, it, hs); });
+    prefix_and_sample<G, D, E, NT>(p, it, L, smem, epoch, kSpinLimit);
+    finish_output<G, D, NT>(p, it);
+}
+
+// Four waves per SIMD (all 1024 splits of a batch-1, 8-KV-head, 32k-token
+// step resident at once) where that fits without spilling registers.
+template <int G, int D, typename E, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
+void fused_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t epoch = next_epoch(read_epoch(p));
+    unsigned int prev = 0;
+    if (threadIdx.x == 0) prev = arrive(p);
+    fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), epoch, smem);
+    if (threadIdx.x == 0) finish_arrival(p, prev, epoch);
+}
+
+template <int G, int D, typename E>
+static const void* fused_fn() {
+    return reinterpret_cast<const void*>(&fused_kernel<G, D, E, kThreads>);
+}
+
+template <int D, typename E>
+static const void* fused_fn_g(int G) {
+    switch (G) {
+        case 1: return fused_fn<1, D, E>();
+        case 2: return fused_fn<2, D, E>();
+        case 4: return fused_fn<4, D, E>();
+        case 7: return fused_fn<7, D, E>();
+        case 8: return fused_fn<8, D, E>();
+        default: return nullptr;
+    }
+}
+
+static const void* fused_function(const Params& p, int dtype) {
+    if (dtype == 0) return p.D == 64 ? fused_fn_g<64, Bf16>(p.G) : fused_fn_g<128, Bf16>(p.G);
+    return p.D == 64 ? fused_fn_g<64, F32>(p.G) : fused_fn_g<128, F32>(p.G);
+}
+
+hipError_t launch_fused(const Params& p, int dtype, hipStream_t stream) {
+    const void* fn = fused_function(p, dtype);
+    if (!fn) return hipErrorInvalidValue;
+    const size_t lds = split_lds_bytes(p.G, p.D, p.split, kThreads);
+    const hipError_t e = allow_lds(fn, lds);
+    if (e != hipSuccess) return e;
+    void* args[] = {const_cast<Params*>(&p)};
+    return hipLaunchKernel(fn, dim3((unsigned)p.items), dim3(kThreads), args, lds, stream);
+}
+
+int fused_blocks_per_cu(const Params& p, int dtype) {
+    const void* fn = fused_function(p, dtype);
+    if (!fn) return 0;
+    const size_t lds = split_lds_bytes(p.G, p.D, p.split, kThreads);
+    if (allow_lds(fn, lds) != hipSuccess) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, lds) != hipSuccess) return 0;
+    return n;
+}
+
+}  // namespace santa

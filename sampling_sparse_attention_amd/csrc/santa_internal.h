@@ -1,5 +1,5 @@
 // Internal launch interface of libsanta: the host-validated parameter block
-// handed by value to every kernel, and the launchers.
+// handed by value to every kernel, the workspace layout and the launchers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,19 +7,52 @@
 
 namespace santa {
 
-// Per split of a query head: maximum scaled score and sum of exp(s - m).
-struct __align__(16) SplitStat {
-    float m;
-    float pad;
-    double l;
-};
-
-constexpr int kBlock = 256;          // threads per workgroup (4 waves of 64)
-constexpr int kWaves = kBlock / 64;
-constexpr int kTargetChunk = 256;    // targets per merge-path pass of one wave
 constexpr int kMaxSplit = 1024;
+constexpr int kRecPerLane = 8;           // split records per lane when a wave merges a sequence's splits
+constexpr int kMaxSplitsPerSeq = 64 * kRecPerLane;   // T: splits of one sequence
 constexpr int kMaxSamples = 65535;
 constexpr int kMaxSortSamples = 8192;
+constexpr int kTargetChunk = 256;        // targets per merge-path pass of one wave
+constexpr int kSpinLimit = 1 << 21;      // polls of a bounded wait (about 1 us each)
+
+// Workspace synchronisation words (first kSyncBytes bytes of the workspace),
+// zero before the first call and left valid by every completed call.
+//   epoch:  epoch of the last call that published split records; a call that
+//           publishes uses epoch + 1 and stores it here once every one of its
+//           workgroups has read the old value;
+//   error:  nonzero once a bounded wait gave up (outputs of that call invalid);
+//   done:   arrival slots that have seen all of their workgroups this call;
+//   arrive: per-slot counts of workgroups that have read the epoch this call
+//           (workgroup w uses slot w % kArriveSlots; one 128-byte line per
+//           slot, so the counting atomics never queue on one address).
+constexpr int kArriveSlots = 64;
+constexpr int kArriveStride = 32;        // 32-bit words between slots
+struct SyncWords {
+    unsigned int epoch;
+    unsigned int error;
+    unsigned int done;
+    unsigned int pad[kArriveStride - 3];
+    unsigned int arrive[kArriveSlots * kArriveStride];
+};
+constexpr size_t kSyncBytes = sizeof(SyncWords);
+
+// Per (sequence, KV head) synchronisation lines (128 bytes each), all zero
+// between calls:
+//   line 0 word 0: splits that have published their records this call (the
+//                  last one resets it);
+//   line 1 word 0: splits that have added their output this call (the last one
+//                  finishes the output and clears the group's state);
+//   lines 2 .. 1+kFlagCopies: copies of a flag raised to the call's epoch once
+//                  all splits published (a waiting workgroup polls copy
+//                  blockIdx % kFlagCopies, so no line is polled by many).
+constexpr int kFlagCopies = 16;
+constexpr int kBarrierLines = 2 + kFlagCopies;
+constexpr int kBarrierStride = 32 * kBarrierLines;   // 32-bit words per (sequence, KV head)
+
+// Partial outputs: each split adds its per-head sums into accumulation slot
+// (split % kOutSlots) of its (sequence, KV head), so few additions meet on one
+// word; the last split to finish sums the slots into o and clears them.
+constexpr int kOutSlots = 16;
 
 struct Params {
     const void* q;
@@ -29,13 +62,16 @@ struct Params {
     const int32_t* block_table;   // null when contiguous
     float* o;
     int32_t* idx;
-    float* scores;                // [B, Hq, score_row]
-    SplitStat* stats;             // [B, Hq, T]
-    double* targets;              // [B, Hq, S] (multinomial only)
+    SyncWords* sync;
+    unsigned long long* records;  // [B, Hq, T] x 2 words: (epoch << 32 | m bits), (epoch << 32 | l bits)
+    unsigned int* barrier;        // [B * Hkv] x kBarrierStride words: counts, epoch flags
+    float* accum;                 // [B * Hkv][kOutSlots][G * D] partial outputs (zero between calls)
+    float* stash;                 // [B, Hq, T * split] scaled scores (two-kernel path)
+    double* targets;              // [B, Hq, S] sorted uniforms (multinomial only)
     int64_t stride_seq;           // elements
     int64_t stride_tok;
     int64_t stride_head;
-    int64_t score_row;            // floats per (b, h) row of the score stash (T * split)
+    int64_t stash_row;            // floats per (b, h) row of the stash (T * split)
     uint64_t seed;
     float scale;                  // 1 / sqrt(d)
     int32_t B, Hq, Hkv, G, D;
@@ -45,31 +81,33 @@ struct Params {
     int32_t num_pages;
     int32_t split;                // keys per split, multiple of 64
     int32_t T;                    // splits per sequence: ceil(n_max / split)
+    int32_t items;                // B * Hkv * T work items (one workgroup each)
     int32_t S;
     int32_t mode;
 };
 
-// Bytes of dynamic LDS each kernel needs.
-size_t score_lds_bytes(int G, int split);
-size_t sample_lds_bytes(int G, int D, int split);
+// Dynamic LDS bytes of the split kernels for a group size, head dim, split and
+// block size.
+size_t split_lds_bytes(int G, int D, int split, int nt);
 size_t sort_lds_bytes(int S);
+
+// Number of threads per workgroup of the split kernels.
+constexpr int kThreads = 256;
 
 hipError_t launch_targets(const Params& p, hipStream_t stream);
 hipError_t launch_score(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_sample(const Params& p, int dtype, hipStream_t stream);
+hipError_t launch_fused(const Params& p, int dtype, hipStream_t stream);
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream);
+// Workgroups of the fused kernel one compute unit can hold at once (0 on error).
+int fused_blocks_per_cu(const Params& p, int dtype);
+// Bytes of LDS one workgroup may use on gfx950.
+constexpr size_t kLdsPerWorkgroup = 163840;
 
-// Element offset of row (token i, KV head g) of sequence b; page entries are
-// clamped into the cache so that a bad table cannot address outside it.
-__device__ __forceinline__ int64_t row_offset(const Params& p, int b, int g, int i) {
-    int64_t off;
-    if (p.page_shift < 0) {
-        off = (int64_t)b * p.stride_seq + (int64_t)i * p.stride_tok;
-    } else {
-        int pg = p.block_table[(int64_t)b * p.pages_per_seq + (i >> p.page_shift)];
-        pg = min(max(pg, 0), p.num_pages - 1);
-        off = (int64_t)pg * p.stride_seq + (int64_t)(i & ((1 << p.page_shift) - 1)) * p.stride_tok;
-    }
-    return off + (int64_t)g * p.stride_head;
+// Lets kernel `fn` be launched with `bytes` of dynamic LDS (needed above 64 KiB).
+inline hipError_t allow_lds(const void* fn, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 // Number of valid tokens of sequence b.

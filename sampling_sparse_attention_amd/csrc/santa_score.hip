@@ -1,142 +1,59 @@
-// Score pass of SANTA decode ("Stochastic Sparse Attention for Memory-Bound
-// Inference", §3.2, Pass 1: exact scores, a score stash, per-tile partition
-// functions), and the sorted targets of multinomial sampling.
-//
-// Work unit: one workgroup per (sequence b, KV head g, split t of `split`
-// consecutive keys).  The G query heads of the group are served from a single
-// read of every K row: the pass streams K with 16-byte loads (LPR lanes per
-// row), forms per-lane partial dot products for R rows x G heads with bf16
-// dot2 (or fp32 FMA) instructions, and finishes them with one reduce-scatter
-// across the row's lanes (DPP), so each lane ends up owning whole scores.
-// Scores go to LDS, then to the stash with coalesced stores, together with the
-// split statistics m = max s and l = sum exp(s - m) (exact fixed-point sum).
-#include "santa_device.h"
-#include "santa_internal.h"
+// Score pass of the two-kernel path ("Stochastic Sparse Attention for
+// Memory-Bound Inference", section 3.2, Pass 1: exact scores, a score stash and
+// per-tile partition functions), the sorted targets of multinomial sampling,
+// and the workspace clear.
+#include "santa_split.h"
 
 namespace santa {
 
-size_t score_lds_bytes(int G, int split) { return (size_t)G * split * sizeof(float); }
+size_t split_lds_bytes(int G, int D, int split, int nt) { return lds_layout(G, D, split, nt).total; }
+
 size_t sort_lds_bytes(int S) {
     int n = 1;
     while (n < S) n <<= 1;
     return (size_t)n * sizeof(uint64_t);
 }
 
-template <int G, int D, typename E>
-__global__ __launch_bounds__(kBlock) void score_kernel(Params p) {
-    constexpr int LPR = D * E::bytes / 16;        // lanes per K row (16 bytes each)
-    constexpr int RPL = 64 / LPR;                 // rows per wave-wide load
-    constexpr int R = 16 / RPL;                   // loads per lane per 16-row chunk
-    constexpr int NV = R * G;                     // partial sums per lane
-    constexpr int NVP = (NV + LPR - 1) / LPR * LPR;
-    constexpr int M = NVP / LPR;                  // finished scores per lane
-    static_assert(LPR >= 2 && LPR <= 32 && 16 % RPL == 0, "row shape");
-
-    extern __shared__ float sc[];                 // [G][split]
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int t = blockIdx.x % p.T;
-    const int bg = blockIdx.x / p.T;
-    const int g = bg % p.Hkv;
-    const int b = bg / p.Hkv;
-    const int n = seq_len_of(p, b);
-
-    if (t == 0) {   // the sample pass accumulates into o
-        float* o = p.o + ((int64_t)b * p.Hq + (int64_t)g * G) * D;
-        for (int i = tid; i < G * D; i += kBlock) o[i] = 0.0f;
-    }
-    const int key0 = t * p.split;
-    if (key0 >= n) return;
-    const int ns = min(p.split, n - key0);
-
-    const int c = lane / LPR;                     // which row of a wave-wide load
-    const int li = lane % LPR;                    // which 16 bytes of the row
-    uint4 qf[G];
-    {
-        const char* qb = reinterpret_cast<const char*>(p.q) +
-                         (((int64_t)b * p.Hq + (int64_t)g * G) * D) * E::bytes + li * 16;
-#pragma unroll
-        for (int h = 0; h < G; ++h) qf[h] = load16(qb + (int64_t)h * D * E::bytes);
-    }
-
-    const char* kbase = reinterpret_cast<const char*>(p.k);
-    const int nchunks = (ns + 15) >> 4;
-
-    auto load_chunk = [&](int ch, uint4* kd) {
-        const int r0 = key0 + (ch << 4);
-        // a 16-row chunk never straddles a page (page_size >= 16, r0 % 16 == 0)
-        const int64_t base = row_offset(p, b, g, r0);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int rr = r * RPL + c;
-            if ((ch << 4) + rr < ns) {
-                kd[r] = load16(kbase + (base + (int64_t)rr * p.stride_tok) * E::bytes + li * 16);
-            } else {
-                kd[r] = make_uint4(0u, 0u, 0u, 0u);
+template <int G, int D, typename E, int NT>
+__global__ __launch_bounds__(NT) void score_kernel(Params p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const uint32_t epoch = next_epoch(read_epoch(p));
+    unsigned int prev = 0;
+    if (threadIdx.x == 0) prev = arrive(p);
+    const Item it = make_item(p, blockIdx.x);
+    if (it.ns != 0) {
+        const LdsLayout L = lds_layout(G, D, p.split, NT);
+        float* sc = reinterpret_cast<float*>(smem + L.scratch);
+        int* pages = reinterpret_cast<int*>(smem + L.pages);
+        HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
+        load_pages<NT>(p, it, pages);
+        __syncthreads();
+        stream_scores<G, D, E, NT>(p, it, sc, pages);
+        __syncthreads();
+        split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
+        __syncthreads();
+        publish_stats<G>(p, it, hs, epoch);
+        // the stash: scaled scores of the split, coalesced 16-byte stores
+        constexpr int NW = NT / 64;
+        const int lane = threadIdx.x & 63;
+        for (int h = threadIdx.x >> 6; h < G; h += NW) {
+            const float* row = sc + h * p.split;
+            float* dst = p.stash + ((int64_t)it.b * p.Hq + it.g * G + h) * p.stash_row + it.key0;
+            for (int i = lane * 4; i < it.ns; i += 256) {
+                if (i + 4 <= it.ns) {
+                    *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(row + i);
+                } else {
+                    for (int e = i; e < it.ns; ++e) dst[e] = row[e];
+                }
             }
         }
-    };
-
-    uint4 cur[R], nxt[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) nxt[r] = make_uint4(0u, 0u, 0u, 0u);
-    if (wave < nchunks) load_chunk(wave, cur);
-    for (int ch = wave; ch < nchunks; ch += kWaves) {
-        if (ch + kWaves < nchunks) load_chunk(ch + kWaves, nxt);
-        float acc[NVP];
-#pragma unroll
-        for (int j = 0; j < NVP; ++j) acc[j] = 0.0f;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int h = 0; h < G; ++h) acc[r * G + h] = E::dot16(cur[r], qf[h], 0.0f);
-        row_reduce_scatter<LPR, NVP>(acc, li);
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            const int vi = li * M + j;
-            if (vi < NV) {
-                const int r = vi / G;
-                const int h = vi - r * G;
-                const int local = (ch << 4) + r * RPL + c;
-                if (local < ns) sc[h * p.split + local] = acc[j] * p.scale;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r) cur[r] = nxt[r];
     }
-    __syncthreads();
-
-    for (int h = wave; h < G; h += kWaves) {
-        const float* row = sc + h * p.split;
-        float mx = -INFINITY;
-        for (int i = lane; i < ns; i += 64) mx = fmaxf(mx, row[i]);
-        mx = wave_max_f32(mx);
-        uint64_t lf = 0;
-        for (int i = lane; i < ns; i += 64) lf += fixed_mass(mass_exp(row[i] - mx));
-        const double l = (double)wave_sum_u64(lf) * kFixedUnit;
-        const int hq = g * G + h;
-        float* dst = p.scores + ((int64_t)b * p.Hq + hq) * p.score_row + key0;
-        for (int i = lane * 4; i < ns; i += 256) {
-            if (i + 4 <= ns) {
-                *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(row + i);
-            } else {
-                for (int e = i; e < ns; ++e) dst[e] = row[e];
-            }
-        }
-        if (lane == 0) {
-            SplitStat st;
-            st.m = mx;
-            st.pad = 0.0f;
-            st.l = l;
-            p.stats[((int64_t)b * p.Hq + hq) * p.T + t] = st;
-        }
-    }
+    if (threadIdx.x == 0) finish_arrival(p, prev, epoch);
 }
 
 // Multinomial targets: the S uniforms of every (sequence, query head), sorted
 // ascending (bitonic sort of their 53-bit integers in LDS), stored as fp64.
-__global__ __launch_bounds__(kBlock) void targets_kernel(Params p) {
+__global__ __launch_bounds__(256) void targets_kernel(Params p) {
     extern __shared__ uint64_t keys[];
     const int bh = blockIdx.x;
     const int b = bh / p.Hq;
@@ -144,7 +61,7 @@ __global__ __launch_bounds__(kBlock) void targets_kernel(Params p) {
     if (seq_len_of(p, b) == 0) return;
     int N = 1;
     while (N < p.S) N <<= 1;
-    for (int j = threadIdx.x; j < N; j += kBlock) {
+    for (int j = threadIdx.x; j < N; j += 256) {
         keys[j] = (j < p.S) ? (philox4x64_10_word0((uint64_t)j, (uint64_t)h, (uint64_t)b, 0ull,
                                                     p.seed, 0ull) >> 11)
                             : ~0ull;
@@ -152,7 +69,7 @@ __global__ __launch_bounds__(kBlock) void targets_kernel(Params p) {
     __syncthreads();
     for (int k = 2; k <= N; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < N; i += kBlock) {
+            for (int i = threadIdx.x; i < N; i += 256) {
                 const int ixj = i ^ j;
                 if (ixj > i) {
                     const uint64_t a = keys[i], c = keys[ixj];
@@ -167,17 +84,32 @@ __global__ __launch_bounds__(kBlock) void targets_kernel(Params p) {
         }
     }
     double* dst = p.targets + (int64_t)bh * p.S;
-    for (int j = threadIdx.x; j < p.S; j += kBlock) dst[j] = (double)keys[j] * 0x1p-53;
+    for (int j = threadIdx.x; j < p.S; j += 256) dst[j] = (double)keys[j] * 0x1p-53;
 }
 
-// ---------------------------------------------------------------------------
-// Launchers
-// ---------------------------------------------------------------------------
+// Zero-fills `n16` 16-byte words and `tail` further bytes.
+__global__ __launch_bounds__(256) void clear_kernel(uint4* p, size_t n16, unsigned char* tail, int ntail) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream) {
+    const size_t n16 = bytes / 16;
+    const int ntail = (int)(bytes % 16);
+    const size_t blocks = n16 ? ((n16 + 255) / 256 < 4096 ? (n16 + 255) / 256 : 4096) : 1;
+    hipLaunchKernelGGL(clear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(ws), n16, reinterpret_cast<unsigned char*>(ws) + n16 * 16,
+                       ntail);
+    return hipGetLastError();
+}
+
 template <int G, int D, typename E>
 static hipError_t launch_score_t(const Params& p, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)p.B * p.Hkv * p.T));
-    hipLaunchKernelGGL((score_kernel<G, D, E>), grid, dim3(kBlock), score_lds_bytes(G, p.split),
-                       stream, p);
+    const size_t lds = split_lds_bytes(G, D, p.split, kThreads);
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(&score_kernel<G, D, E, kThreads>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((score_kernel<G, D, E, kThreads>), dim3((unsigned)p.items), dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
 
@@ -200,8 +132,8 @@ hipError_t launch_score(const Params& p, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_targets(const Params& p, hipStream_t stream) {
-    const dim3 grid((unsigned)((int64_t)p.B * p.Hq));
-    hipLaunchKernelGGL(targets_kernel, grid, dim3(kBlock), sort_lds_bytes(p.S), stream, p);
+    hipLaunchKernelGGL(targets_kernel, dim3((unsigned)((int64_t)p.B * p.Hq)), dim3(256),
+                       sort_lds_bytes(p.S), stream, p);
     return hipGetLastError();
 }
 

@@ -1,0 +1,837 @@
+// The phases of one SANTA work item -- one (sequence b, KV head g, split t of
+// `split` consecutive keys) -- shared by the fused decode kernel and by the
+// two-kernel path (score pass + sample pass).
+//
+//   stream_scores  exact scores q_h . k_i / sqrt(d) of the split's keys for the
+//                  G query heads of the group, from one read of every K row
+//                  ("Stochastic Sparse Attention for Memory-Bound Inference",
+//                  section 2, Eq. 1; section 3.2, Pass 1);
+//   split_stats    per head: the split's maximum m_t, the fixed-point masses
+//                  e_i = exp(s_i - m_t), their in-split prefix P_i and total
+//                  l_t (the tile partition function of section 3.2, Pass 1);
+//   publish_stats  writes (m_t, l_t) for the other workgroups of the sequence;
+//   group_barrier  waits until every split of the sequence has published;
+//   prefix_and_sample
+//                  per head (one wave): merges the splits' statistics to a
+//                  common maximum M (online softmax merge), forms the exact
+//                  prefix W of split masses and the total Z (the global
+//                  partition function of section 3.2, step 2) and the range of
+//                  targets this split owns, then samples them by inverse CDF
+//                  (section 2.1 and Appendix A.4) with a merge path against
+//                  the split's CDF and gathers-and-adds the sampled V rows
+//                  with duplicates counted (section 2, Eq. 2-3).
+#pragma once
+
+#include "santa_device.h"
+#include "santa_internal.h"
+
+namespace santa {
+
+struct Item {
+    int b, g, t;   // sequence, KV head, split
+    int n;         // tokens of sequence b
+    int key0;      // first key of the split
+    int ns;        // keys in the split (0: past the end of the sequence)
+    int Tb;        // splits of sequence b
+};
+
+__device__ __forceinline__ Item make_item(const Params& p, int item) {
+    Item it;
+    it.t = item % p.T;
+    const int grp = item / p.T;
+    it.g = grp % p.Hkv;
+    it.b = grp / p.Hkv;
+    it.n = seq_len_of(p, it.b);
+    it.key0 = it.t * p.split;
+    it.ns = max(0, min(p.split, it.n - it.key0));
+    it.Tb = (it.n + p.split - 1) / p.split;
+    return it;
+}
+
+// Per query head of the work item, kept in LDS.
+struct HeadState {
+    double w_lo;    // mass of the sequence's splits before this one (W_t)
+    double z;       // total mass Z of the sequence
+    double f;       // exp(m_t - M)
+    double u0;      // systematic offset
+    float m_t;      // this split's maximum score
+    float l_t;      // this split's mass, sum of exp(s_i - m_t)
+    int m_lo;       // targets [m_lo, m_hi) fall into this split
+    int m_hi;
+    int lastpos;    // last key of positive mass in the split
+    int pad[3];
+};
+
+// Byte offsets of the dynamic LDS of a split workgroup.
+struct LdsLayout {
+    uint32_t scratch;   // scores fp32 [G][split]; after the statistics, per wave
+                        // a TargetArea (merge targets and the sampled-key list)
+    uint32_t prefix;    // u64 [G][split] in-split inclusive prefix of fixed-point masses
+    uint32_t pages;     // int [split/16 + 1] physical pages of the split (paged caches)
+    uint32_t heads;     // HeadState [G]
+    uint32_t total;
+};
+
+// Per wave, for one chunk of at most kTargetChunk targets of one head.
+struct TargetArea {
+    double tau[kTargetChunk];      // targets scaled by Z
+    int key[kTargetChunk];         // split-local key of each target (merge path)
+    int lkey[kTargetChunk];        // distinct sampled keys, ascending
+    unsigned int lcnt[kTargetChunk];   // samples of each of them
+};
+
+__host__ __device__ inline LdsLayout lds_layout(int G, int D, int split, int nt) {
+    const int nw = nt / 64;
+    size_t scratch = (size_t)G * split * 4;
+    if ((size_t)nw * sizeof(TargetArea) > scratch) scratch = (size_t)nw * sizeof(TargetArea);
+    LdsLayout L;
+    L.scratch = 0;
+    L.prefix = (uint32_t)((scratch + 15) & ~(size_t)15);
+    L.pages = L.prefix + (uint32_t)(G * split * 8);
+    L.heads = (L.pages + (uint32_t)((split / 16 + 1) * 4) + 15) & ~15u;
+    L.total = L.heads + (uint32_t)(G * sizeof(HeadState));
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// KV rows
+// ---------------------------------------------------------------------------
+
+// Physical pages of the split's keys (paged caches), clamped into the cache so
+// that a bad table entry cannot address outside it.
+template <int NT>
+__device__ __forceinline__ void load_pages(const Params& p, const Item& it, int* pages) {
+    if (p.page_shift < 0 || it.ns == 0) return;
+    const int first = it.key0 >> p.page_shift;
+    const int last = (it.key0 + it.ns - 1) >> p.page_shift;
+    const int32_t* bt = p.block_table + (int64_t)it.b * p.pages_per_seq;
+    for (int k = threadIdx.x; k <= last - first; k += NT) {
+        const int pg = bt[first + k];
+        pages[k] = min(max(pg, 0), p.num_pages - 1);
+    }
+}
+
+// Element offset of key `local` of the split (KV head g included).
+__device__ __forceinline__ int64_t row_offset(const Params& p, const Item& it, int local,
+                                              const int* pages) {
+    const int key = it.key0 + local;
+    int64_t off;
+    if (p.page_shift < 0) {
+        off = (int64_t)it.b * p.stride_seq + (int64_t)key * p.stride_tok;
+    } else {
+        const int pg = pages[(key >> p.page_shift) - (it.key0 >> p.page_shift)];
+        off = (int64_t)pg * p.stride_seq + (int64_t)(key & ((1 << p.page_shift) - 1)) * p.stride_tok;
+    }
+    return off + (int64_t)it.g * p.stride_head;
+}
+
+// ---------------------------------------------------------------------------
+// Scores: stream the split's K rows once for all G heads.
+// A K row of d elements is read by LPR = d*e/16 lanes with 16-byte loads; a
+// wave-wide load covers RPL = 64/LPR rows, and a 16-row chunk takes R = 16/RPL
+// loads per lane.  A wave issues the loads of CB chunks (16 loads per lane)
+// before using any of them.  Each lane forms R*G partial dot products; a
+// reduce-scatter across the row's lanes leaves every lane owning whole scores.
+// ---------------------------------------------------------------------------
+template <int G, int D, typename E, int NT>
+__device__ __forceinline__ void stream_scores(const Params& p, const Item& it, float* sc,
+                                              const int* pages) {
+    constexpr int NW = NT / 64;
+    constexpr int LPR = D * E::bytes / 16;
+    constexpr int RPL = 64 / LPR;
+    constexpr int R = 16 / RPL;
+    constexpr int CB = (16 / R) > 0 ? 16 / R : 1;
+    constexpr int NV = R * G;
+    constexpr int NVP = (NV + LPR - 1) / LPR * LPR;
+    constexpr int M = NVP / LPR;
+    static_assert(LPR >= 2 && LPR <= 32 && 16 % RPL == 0, "row shape");
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane / LPR;
+    const int li = lane % LPR;
+    const int split = p.split;
+
+    uint4 qf[G];
+    {
+        const char* qb = reinterpret_cast<const char*>(p.q) +
+                         (((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D) * E::bytes + li * 16;
+#pragma unroll
+        for (int h = 0; h < G; ++h) qf[h] = load16(qb + (int64_t)h * D * E::bytes);
+    }
+    const char* kbase = reinterpret_cast<const char*>(p.k);
+    const int nchunks = (it.ns + 15) >> 4;
+
+    for (int base = wave; base < nchunks; base += NW * CB) {
+        uint4 kd[CB][R];
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            const int ch = base + k * NW;
+            const int r0 = ch << 4;
+            // a 16-row chunk never straddles a page (pages >= 16 rows, r0 % 16 == 0)
+            const int64_t off = (ch < nchunks) ? row_offset(p, it, r0, pages) : 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int rr = r * RPL + c;
+                if (ch < nchunks && r0 + rr < it.ns) {
+                    kd[k][r] = load16(kbase + (off + (int64_t)rr * p.stride_tok) * E::bytes + li * 16);
+                } else {
+                    kd[k][r] = make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            const int ch = base + k * NW;
+            if (ch < nchunks) {
+                float acc[NVP];
+#pragma unroll
+                for (int j = 0; j < NVP; ++j) acc[j] = 0.0f;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[r * G + h] = E::dot16(kd[k][r], qf[h], 0.0f);
+                row_reduce_scatter<LPR, NVP>(acc, li);
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    const int vi = li * M + j;
+                    if (vi < NV) {
+                        const int r = vi / G;
+                        const int h = vi - r * G;
+                        const int local = (ch << 4) + r * RPL + c;
+                        if (local < it.ns) sc[h * split + local] = acc[j] * p.scale;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split statistics and the in-split prefix (one wave per head).  Lane L owns
+// keys [L*ept, (L+1)*ept), ept = split/64 <= 16; the loops over them stay
+// rolled (short, data-dependent trip counts).
+// ---------------------------------------------------------------------------
+template <int G, int NT>
+__device__ __forceinline__ void split_stats(const Params& p, const Item& it, const float* sc,
+                                            uint64_t* prefix, HeadState* hs) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int split = p.split;
+    const int ept = split >> 6;
+    const int i0 = lane * ept;
+    const int n_own = max(0, min(ept, it.ns - i0));    // keys of this lane inside the split
+    for (int h = wave; h < G; h += NW) {
+        const float* row = sc + h * split + i0;
+        uint64_t* ph = prefix + h * split + i0;
+        float mx = -INFINITY;
+#pragma unroll 4
+        for (int k = 0; k < n_own; ++k) mx = fmaxf(mx, row[k]);
+        mx = wave_max_f32(mx);
+        // fixed-point masses and their in-lane inclusive prefix
+        uint64_t run = 0;
+        int lastpos = -1;
+#pragma unroll 4
+        for (int k = 0; k < n_own; ++k) {
+            const uint64_t e = fixed_mass(mass_exp(row[k] - mx));
+            if (e) lastpos = i0 + k;
+            run += e;
+            ph[k] = run;
+        }
+        const uint64_t incl = wave_scan_add_u64(run);
+        const uint64_t excl = incl - run;
+#pragma unroll 4
+        for (int k = 0; k < n_own; ++k) ph[k] += excl;
+        const uint64_t total = lane_u64(incl, 63);
+        lastpos = wave_max_i32(lastpos);
+        if (lane == 0) {
+            hs[h].m_t = mx;
+            hs[h].l_t = (float)fixed_to_double(total);
+            hs[h].lastpos = lastpos;
+        }
+    }
+}
+
+// The systematic offsets U of the item's G heads, by the wave WAVE (lane h
+// for head h); they depend on nothing the other splits compute.
+template <int G, int WAVE>
+__device__ __forceinline__ void systematic_offsets(const Params& p, const Item& it, HeadState* hs) {
+    if (p.mode == 2 && (threadIdx.x >> 6) == WAVE) {
+        const int lane = threadIdx.x & 63;
+        const double u0 = uniform01(p.seed, it.b, it.g * G + (lane % G), 0ull);
+        if (lane < G) hs[lane].u0 = u0;
+    }
+}
+
+// Record of split t of query head hq of sequence b: two 64-bit words, each
+// (epoch << 32 | 32 payload bits), written and read as single atomic words.
+__device__ __forceinline__ unsigned long long* record_of(const Params& p, int b, int hq, int t) {
+    return p.records + (((int64_t)b * p.Hq + hq) * p.T + t) * 2;
+}
+
+template <int G>
+__device__ __forceinline__ void publish_stats(const Params& p, const Item& it, const HeadState* hs,
+                                              uint32_t epoch) {
+    const int h = threadIdx.x;
+    if (h < G) {
+        unsigned long long* rec = record_of(p, it.b, it.g * G + h, it.t);
+        const unsigned long long tag = (unsigned long long)epoch << 32;
+        __hip_atomic_store(rec, tag | __float_as_uint(hs[h].m_t), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(rec + 1, tag | __float_as_uint(hs[h].l_t), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Barrier of the Tb splits of one (sequence, KV head) in the fused kernel: a
+// sense-reversing counter.  Each split counts itself in once its records are
+// written; the last one resets the count and raises the flag to this call's
+// epoch; the others poll the flag word alone, so waiting adds almost no
+// memory traffic.  `overlap()` runs on every thread meanwhile (thread 0 after
+// its wait).  Returns false if the bounded wait gave up.
+// ---------------------------------------------------------------------------
+template <typename Overlap>
+__device__ __forceinline__ bool group_barrier(const Params& p, const Item& it, uint32_t epoch,
+                                              Overlap&& overlap) {
+    __shared__ int s_ok;
+    if (threadIdx.x == 0) {
+        unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
+        int ok = 1;
+        const unsigned int prev = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == (unsigned int)it.Tb - 1u) {
+            __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int c = 0; c < kFlagCopies; ++c)
+                __hip_atomic_store(bar + 32 * (2 + c), epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const unsigned int* flag = bar + 32 * (2 + blockIdx.x % kFlagCopies);
+            for (int iter = 0;
+                 __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch; ++iter) {
+                if (iter >= kSpinLimit) {
+                    ok = 0;
+                    __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        s_ok = ok;
+    }
+    overlap();      // the other waves' independent work while thread 0 waits
+    __syncthreads();
+    return s_ok != 0;
+}
+
+// ---------------------------------------------------------------------------
+// Targets of §2 / §2.1 scaled by Z: tau_m = t_m * Z, non-decreasing in m.
+//   multinomial  t_m = m-th smallest of S uniforms (sorted in the workspace);
+//   stratified   t_m = (m + U_m) / S;
+//   systematic   t_m = (m + U_0) / S.
+// Counting and merging use this one function, so both see the same bits.
+// ---------------------------------------------------------------------------
+// MODE is a template argument so that no path evaluates another mode's
+// targets (the compiler would otherwise compute the stratified Philox draw
+// speculatively for every target).
+template <int MODE>
+struct TargetSeq {
+    const double* sorted;
+    double u0;
+    double z;
+    uint64_t seed;
+    int S, b, hq;
+    __device__ __forceinline__ double tau(int m) const {
+        double t;
+        if constexpr (MODE == 0) {
+            t = sorted[m];
+        } else if constexpr (MODE == 1) {
+            t = ((double)m + uniform01(seed, b, hq, (uint64_t)m)) / (double)S;
+        } else {
+            t = ((double)m + u0) / (double)S;
+        }
+        return t * z;
+    }
+};
+
+// Number of m in [0, S) with tau_m < x (tau non-decreasing in m).
+template <int MODE>
+__device__ __forceinline__ int count_below(const TargetSeq<MODE>& ts, double x, int lane) {
+    if constexpr (MODE != 0) {
+        // lane-parallel scan upward in windows of 64 targets
+        for (int base = 0;; base += 64) {
+            const int m = base + lane;
+            const bool below = m < ts.S && ts.tau(m) < x;
+            const unsigned long long bal = __ballot(below);
+            if (bal != ~0ull) return base + __popcll(bal);
+        }
+    } else {
+        // multinomial: 64-ary search over the sorted targets, one probe per lane
+        int lo = 0, hi = ts.S;
+        while (hi > lo) {
+            const int len = hi - lo;
+            const int step = (len + 63) >> 6;
+            const int pos = lo + (lane + 1) * step - 1;
+            const bool below = (pos < hi) && (ts.tau(pos) < x);
+            const int k = __popcll(__ballot(below));
+            if (step == 1) return lo + k;
+            const int nlo = lo + k * step;
+            hi = min(hi, lo + (k + 1) * step - 1);
+            lo = nlo;
+        }
+        return lo;
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ TargetSeq<MODE> target_seq(const Params& p, int b, int hq, double z, double u0) {
+    TargetSeq<MODE> ts;
+    ts.sorted = p.targets + ((int64_t)b * p.Hq + hq) * p.S;
+    ts.seed = p.seed;
+    ts.S = p.S;
+    ts.b = b;
+    ts.hq = hq;
+    ts.u0 = u0;
+    ts.z = z;
+    return ts;
+}
+
+// Targets [m_lo, m_hi) of split t: those with W_t <= tau_m < W_{t+1}; the last
+// split of positive mass also takes targets that round to tau >= Z.  For
+// stratified and systematic targets tau_m lies in stratum m of [0, Z), so the
+// count below x is within one of x * S / Z: lanes 0-31 test the 32 targets
+// around that estimate for W_t, lanes 32-63 those for W_{t+1}, and one ballot
+// gives both counts (a full scan covers a window that misses the boundary).
+template <int MODE>
+__device__ __forceinline__ void target_range(const Params& p, int b, int hq, double z, double u0,
+                                             double w_lo, double w_hi, bool last, int lane,
+                                             int* m_lo, int* m_hi) {
+    const TargetSeq<MODE> ts = target_seq<MODE>(p, b, hq, z, u0);
+    if constexpr (MODE == 0) {
+        *m_lo = count_below(ts, w_lo, lane);
+        *m_hi = last ? p.S : count_below(ts, w_hi, lane);
+    } else {
+        const bool upper = lane >= 32;
+        const double x = upper ? w_hi : w_lo;
+        const double est = x / z * (double)p.S - (MODE == 2 ? u0 : 0.0);
+        const int base = (int)ceil(fmin(fmax(est, -1.0), (double)p.S)) - 16;
+        const int m = base + (lane & 31);
+        // targets below index 0 do not exist: count them as below x, so that
+        // the count is the index of the first target at or above x
+        const bool below = m < 0 || (m < p.S && ts.tau(m) < x);
+        const unsigned long long bal = __ballot(below);
+        const int base_lo = __builtin_amdgcn_readlane(base, 0);
+        const int base_hi = __builtin_amdgcn_readlane(base, 32);
+        const uint32_t lo_bits = (uint32_t)bal, hi_bits = (uint32_t)(bal >> 32);
+        int c_lo = base_lo + __popc(lo_bits);
+        int c_hi = base_hi + __popc(hi_bits);
+        // the window holds the boundary iff its first target is below x and its last is not
+        if (!((lo_bits & 1u) && !(lo_bits >> 31))) c_lo = count_below(ts, w_lo, lane);
+        if (!((hi_bits & 1u) && !(hi_bits >> 31))) c_hi = count_below(ts, w_hi, lane);
+        *m_lo = c_lo;
+        *m_hi = last ? p.S : c_hi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF sampling of targets [m0, m0 + na) of one head (one wave): each
+// target tau goes to the key j with C_j <= tau < C_{j+1} (half-open intervals,
+// Appendix A.4); a target past the split's last edge (rounding) goes to its
+// last key of positive mass.  Writes idx and leaves the distinct keys with
+// their sample counts, ascending, in ta->lkey / ta->lcnt; returns how many.
+//   few targets (<= 8): one at a time -- a ballot over the lanes' last edges finds
+//     the lane that owns the key, one LDS read per lane finds the key;
+//   many: a merge path of targets against edges, lane-parallel, then a
+//     run-length compaction of the keys.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, const HeadState& st, int hq,
+                                            const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
+    const int ns = it.ns;
+    const int ept = p.split >> 6;
+    int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S;
+    const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0);
+    const int lastpos = max(st.lastpos, 0);
+    // upper edge of key j's interval: C_{j+1} = W_t + exp(m_t - M) * P_j
+    auto edge = [&](int j) { return st.w_lo + st.f * fixed_to_double(ph[j]); };
+    int nlist = 0;
+    if (na <= 8) {
+        double my_tau = 0.0;
+        if (lane < na) my_tau = ts.tau(m0 + lane);
+        const int i0 = lane * ept;
+        const int n_own = max(0, min(ept, ns - i0));
+        const double lane_hi = n_own > 0 ? edge(i0 + n_own - 1) : INFINITY;
+        int prev = -1;
+        for (int k = 0; k < na; ++k) {
+            const double t = __shfl(my_tau, k, 64);
+            // lanes whose every key's interval ends at or below t
+            const int c = __popcll(__ballot(lane_hi <= t));
+            int local;
+            if (c * ept >= ns) {
+                local = lastpos;
+            } else {
+                const bool le = lane < ept && c * ept + lane < ns && edge(c * ept + lane) <= t;
+                local = c * ept + __popcll(__ballot(le));
+            }
+            if (lane == 0) {
+                idx_row[m0 + k] = it.key0 + local;
+                if (local == prev) {
+                    ta->lcnt[nlist - 1] += 1u;
+                } else {
+                    ta->lkey[nlist] = local;
+                    ta->lcnt[nlist] = 1u;
+                }
+            }
+            if (local != prev) ++nlist;
+            prev = local;
+        }
+        wave_lds_sync();
+        return nlist;
+    }
+    for (int k = lane; k < na; k += 64) ta->tau[k] = ts.tau(m0 + k);
+    wave_lds_sync();
+    // lane takes an equal share of the merged sequence; an edge equal to a
+    // target comes first, so the target goes to the key above it
+    const int total = na + ns;
+    const int per = (total + 63) >> 6;
+    const int d0 = min(lane * per, total);
+    const int d1 = min(d0 + per, total);
+    int lo = max(0, d0 - ns), up = min(d0, na);
+    while (lo < up) {
+        const int mid = (lo + up) >> 1;
+        if (ta->tau[mid] < edge(d0 - 1 - mid)) lo = mid + 1;
+        else up = mid;
+    }
+    int i = lo, j = d0 - lo;
+    for (int d = d0; d < d1; ++d) {
+        if (i < na && (j >= ns || ta->tau[i] < edge(j))) {
+            const int local = (j < ns) ? j : lastpos;
+            idx_row[m0 + i] = it.key0 + local;
+            ta->key[i] = local;
+            ++i;
+        } else {
+            ++j;
+        }
+    }
+    wave_lds_sync();
+    // run-length compaction of the (non-decreasing) keys: first the start of
+    // every run, then each run's length from the start of the next
+    for (int c0 = 0; c0 < na; c0 += 64) {
+        const int m = c0 + lane;
+        const bool start = m < na && (m == 0 || ta->key[m - 1] != ta->key[m]);
+        const unsigned long long starts = __ballot(start);
+        if (start) {
+            const int pos = nlist + __popcll(starts & ((1ull << lane) - 1ull));
+            ta->lkey[pos] = ta->key[m];
+            ta->lcnt[pos] = (unsigned)m;
+        }
+        nlist += __popcll(starts);
+    }
+    wave_lds_sync();
+    for (int q0 = 0; q0 < nlist; q0 += 64) {
+        const int q = q0 + lane;
+        unsigned int len = 0;
+        if (q < nlist) {
+            const unsigned int next = (q + 1 < nlist) ? ta->lcnt[q + 1] : (unsigned)na;
+            len = next - ta->lcnt[q];
+        }
+        wave_lds_sync();
+        if (q < nlist) ta->lcnt[q] = len;
+        wave_lds_sync();
+    }
+    wave_lds_sync();
+    return nlist;
+}
+
+// ---------------------------------------------------------------------------
+// Sampling and gather-and-add for one head (one wave, no workgroup barrier).
+// Each distinct sampled key of a chunk of targets is gathered once, a whole V
+// row per wave-wide load (lane l holds elements [l*EL, (l+1)*EL)), weighted
+// by its sample count; all of a chunk's loads are issued before any is used.
+// The waves of a workgroup gather the rows of the same split at the same
+// time, so a row that several heads of the group sampled is fetched from HBM
+// once and served to the others from L2.
+// ---------------------------------------------------------------------------
+template <int G, int D, typename E>
+__device__ __forceinline__ void sample_head(const Params& p, const Item& it, const HeadState& st, int h,
+                                            const LdsLayout& L, unsigned char* smem) {
+    constexpr int EL = D / 64;                  // elements of a V row per lane
+    constexpr int U = 8;                        // rows in flight per wave
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int hq = it.g * G + h;
+    const uint64_t* ph = reinterpret_cast<const uint64_t*>(smem + L.prefix) + h * p.split;
+    const int* pages = reinterpret_cast<const int*>(smem + L.pages);
+    TargetArea* ta = reinterpret_cast<TargetArea*>(smem + L.scratch) + wave;
+    const char* vbase = reinterpret_cast<const char*>(p.v);
+
+    float acc[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = 0.0f;
+    for (int m0 = st.m_lo; m0 < st.m_hi; m0 += kTargetChunk) {
+        const int na = min(kTargetChunk, st.m_hi - m0);
+        int nlist;
+        if (p.mode == 2) nlist = sample_chunk<2>(p, it, st, hq, ph, ta, m0, na, lane);
+        else if (p.mode == 1) nlist = sample_chunk<1>(p, it, st, hq, ph, ta, m0, na, lane);
+        else nlist = sample_chunk<0>(p, it, st, hq, ph, ta, m0, na, lane);
+        for (int r0 = 0; r0 < nlist; r0 += U) {
+            float x[U][EL];
+            float wgt[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                wgt[u] = 0.0f;
+#pragma unroll
+                for (int e = 0; e < EL; ++e) x[u][e] = 0.0f;
+                if (r0 + u < nlist) {
+                    const int64_t off = row_offset(p, it, ta->lkey[r0 + u], pages) + lane * EL;
+                    E::template load_row_part<EL>(vbase + off * E::bytes, x[u]);
+                    wgt[u] = (float)ta->lcnt[r0 + u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < EL; ++e) acc[e] = fmaf(wgt[u], x[u][e], acc[e]);
+        }
+        wave_lds_sync();       // the next chunk reuses the target area
+    }
+    float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D +
+                  lane * EL;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slot + e, acc[e]);
+}
+
+// ---------------------------------------------------------------------------
+// Global partition function, this split's target range, then the head's
+// sampling and gather (one wave per head, no workgroup barrier).
+// Split masses w_j = l_j * exp(m_j - M) are summed as fixed point with 2^-40
+// resolution, so the prefix W is exact, monotone and identical in every
+// workgroup of the sequence, and the ranges [W_t, W_t+1) tile [0, Z).
+// Records still missing after `spin_limit` re-reads set the error word.
+// Returns false if the wait gave up.
+// ---------------------------------------------------------------------------
+template <int G, int D, typename E, int NT>
+__device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
+                                                  unsigned char* smem, uint32_t epoch, int spin_limit) {
+    HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int Tb = it.Tb;
+    const int K = (Tb + 63) >> 6;               // records per lane, <= kRecPerLane
+    bool ok_all = true;
+    for (int h = wave; h < G; h += NW) {
+        const int hq = it.g * G + h;
+        const unsigned long long* rec = record_of(p, it.b, hq, 0);
+        float mr[kRecPerLane], lr[kRecPerLane];
+        // first an ordinary (cached) read: after the barrier every record is
+        // normally in place, and the splits' workgroups on one XCD then share
+        // its L2 copy; a record whose epoch does not match yet is re-read
+        // below with device-coherent loads until it does
+        bool fresh = true;
+#pragma unroll
+        for (int k = 0; k < kRecPerLane; ++k) {
+            const int j = lane * K + k;
+            mr[k] = -INFINITY;
+            lr[k] = 0.0f;
+            if (k < K && j < Tb) {
+                const ulonglong2 r = *reinterpret_cast<const ulonglong2*>(rec + 2 * j);
+                fresh &= (uint32_t)(r.x >> 32) == epoch && (uint32_t)(r.y >> 32) == epoch;
+                mr[k] = __uint_as_float((uint32_t)r.x);
+                lr[k] = __uint_as_float((uint32_t)r.y);
+            }
+        }
+        for (int iter = 0; !__all(fresh); ++iter) {
+            bool ok = true;
+#pragma unroll
+            for (int k = 0; k < kRecPerLane; ++k) {
+                const int j = lane * K + k;
+                mr[k] = -INFINITY;
+                lr[k] = 0.0f;
+                if (k < K && j < Tb) {
+                    const unsigned long long a =
+                        __hip_atomic_load(rec + 2 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const unsigned long long w =
+                        __hip_atomic_load(rec + 2 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok &= (uint32_t)(a >> 32) == epoch && (uint32_t)(w >> 32) == epoch;
+                    mr[k] = __uint_as_float((uint32_t)a);
+                    lr[k] = __uint_as_float((uint32_t)w);
+                }
+            }
+            if (__all(ok)) break;
+            if (iter >= spin_limit) {
+                ok_all = false;
+                if (lane == 0)
+                    __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kRecPerLane; ++k) mx = fmaxf(mx, mr[k]);
+        const float M = wave_max_f32(mx);
+        // lane-local exclusive prefix at the positions of splits t and t + 1
+        const int t = it.t;
+        const int kt = t % K;
+        const int kt1 = (t + 1) % K;
+        uint64_t run = 0, at_t = 0, at_t1 = 0;
+        int last = -1;
+#pragma unroll
+        for (int k = 0; k < kRecPerLane; ++k) {
+            const int j = lane * K + k;
+            uint64_t w = 0;
+            if (k < K && j < Tb) {
+                const double f = (double)mass_exp(mr[k] - M);
+                w = (uint64_t)((double)lr[k] * f * 0x1p40);
+                if (w) last = j;
+            }
+            if (k == kt) at_t = run;
+            if (k == kt1) at_t1 = run;
+            run += w;
+        }
+        const uint64_t incl = wave_scan_add_u64(run);
+        const uint64_t excl = incl - run;
+        const uint64_t Z = lane_u64(incl, 63);
+        last = wave_max_i32(last);
+        // W_t and W_{t+1} (exclusive prefixes of splits t and t+1)
+        const uint64_t mine_t = excl + at_t;
+        const uint64_t mine_t1 = excl + at_t1;
+        const uint64_t W_t = lane_u64(mine_t, t / K);
+        const uint64_t W_t1 = (t + 1 < Tb) ? lane_u64(mine_t1, (t + 1) / K) : Z;
+
+        const double u0 = hs[h].u0;
+        const double z = (double)Z * 0x1p-40;
+        const double w_lo = (double)W_t * 0x1p-40;
+        const double w_hi = (double)W_t1 * 0x1p-40;
+        int m_lo, m_hi;
+        if (p.mode == 2) target_range<2>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
+        else if (p.mode == 1) target_range<1>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
+        else target_range<0>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
+        if (lane == 0) {
+            hs[h].w_lo = w_lo;
+            hs[h].z = z;
+            hs[h].f = (double)mass_exp(hs[h].m_t - M);
+            hs[h].m_lo = m_lo;
+            hs[h].m_hi = max(m_hi, m_lo);
+        }
+        wave_lds_sync();
+        const HeadState st = hs[h];
+        if (st.m_hi > st.m_lo) sample_head<G, D, E>(p, it, st, h, L, smem);
+    }
+    return ok_all;
+}
+
+// Waits until every memory operation this wave has issued has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------
+// The output of a (sequence, KV head) and the clean-up of its workspace state.
+// Each split, once its additions into the accumulation slots have completed,
+// counts itself done.  The last one -- every other split of the group has then
+// passed the barrier and read the records and targets -- sums the kOutSlots
+// slots, stores o = (1/S) * sum (Eq. 3) for the G heads, and returns to zero
+// the slots, the epoch flags, the group's split records and (multinomial) its
+// targets, so that a completed call leaves this state all zero.
+// ---------------------------------------------------------------------------
+template <int G, int D, int NT>
+__device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
+    __shared__ int s_last;
+    wait_memory();           // this wave's slot additions have been performed
+    __syncthreads();
+    unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
+    if (threadIdx.x == 0) {
+        const unsigned int prev = __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned int)it.Tb - 1u;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    // slot words in pairs: the 16 loads of a pair are all in flight at once
+    constexpr int NP = G * D / 2;
+    unsigned long long* acc =
+        reinterpret_cast<unsigned long long*>(p.accum + ((int64_t)it.b * p.Hkv + it.g) * kOutSlots * G * D);
+    float* o = p.o + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D;
+    const float inv_s = 1.0f / (float)p.S;
+    for (int i = threadIdx.x; i < NP; i += NT) {
+        unsigned long long v[kOutSlots];
+#pragma unroll
+        for (int k = 0; k < kOutSlots; ++k)
+            v[k] = __hip_atomic_load(acc + k * NP + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kOutSlots; ++k) {
+            s0 += __uint_as_float((uint32_t)v[k]);
+            s1 += __uint_as_float((uint32_t)(v[k] >> 32));
+        }
+#pragma unroll
+        for (int k = 0; k < kOutSlots; ++k)
+            __hip_atomic_store(acc + k * NP + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *reinterpret_cast<float2*>(o + 2 * i) = make_float2(s0 * inv_s, s1 * inv_s);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(bar + 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < kFlagCopies)
+        __hip_atomic_store(bar + 32 * (2 + threadIdx.x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = threadIdx.x; i < G * it.Tb; i += NT) {
+        const int h = i / it.Tb;
+        unsigned long long* r = record_of(p, it.b, it.g * G + h, i - h * it.Tb);
+        __hip_atomic_store(r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(r + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (p.mode == 0) {
+        double* tg = p.targets + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
+        for (int i = threadIdx.x; i < G * p.S; i += NT) tg[i] = 0.0;
+    }
+}
+
+// o = 0 and idx = -1 for the G heads of an empty sequence.
+template <int G, int D, int NT>
+__device__ __forceinline__ void write_empty(const Params& p, const Item& it) {
+    float* o = p.o + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D;
+    for (int i = threadIdx.x; i < G * D; i += NT) o[i] = 0.0f;
+    int32_t* idx = p.idx + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
+    for (int i = threadIdx.x; i < G * p.S; i += NT) idx[i] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// Call epochs.  Every workgroup reads the epoch word once (an uncontended
+// atomic load).  A call that publishes split records uses epoch + 1 and counts
+// its workgroups in: the last of each arrival slot clears the slot and counts
+// the slot done, the last slot stores the new epoch.  The sample pass of the
+// two-kernel path reads the epoch its score pass stored and does not advance.
+// ---------------------------------------------------------------------------
+// The epoch a publishing call uses after `e`; never 0, which marks a record or
+// flag as not written.
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1u == 0u ? 1u : e + 1u; }
+
+__device__ __forceinline__ uint32_t read_epoch(const Params& p) {
+    __shared__ uint32_t s_epoch;
+    if (threadIdx.x == 0)
+        s_epoch = __hip_atomic_load(&p.sync->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return s_epoch;
+}
+
+// Thread 0 only: this workgroup's arrival; returns the count before it.
+__device__ __forceinline__ unsigned int arrive(const Params& p) {
+    const int k = blockIdx.x % kArriveSlots;
+    return __hip_atomic_fetch_add(&p.sync->arrive[k * kArriveStride], 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 only, with the value arrive() returned: the last workgroup of the
+// last slot publishes `epoch` for the next call.
+__device__ __forceinline__ void finish_arrival(const Params& p, unsigned int prev, uint32_t epoch) {
+    const unsigned int k = blockIdx.x % kArriveSlots;
+    const unsigned int slot_size = (gridDim.x - k + kArriveSlots - 1) / kArriveSlots;
+    if (prev != slot_size - 1) return;
+    __hip_atomic_store(&p.sync->arrive[k * kArriveStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int slots = gridDim.x < (unsigned)kArriveSlots ? gridDim.x : (unsigned)kArriveSlots;
+    const unsigned int d = __hip_atomic_fetch_add(&p.sync->done, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    if (d == slots - 1) {
+        __hip_atomic_store(&p.sync->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.sync->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+}  // namespace santa

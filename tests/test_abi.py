@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert len(declared) == 8
+    assert len(declared) == 10
     out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (santa_\w+)", out))
@@ -67,16 +67,30 @@ def test_workspace_layout_llama_shape(lib):
     lay = santa.santa_workspace_layout_query(_shape(), 256, 2)
     T, split = lay.num_splits, lay.split_size
     assert split % 64 == 0 and T * split >= 32768 and (T - 1) * split < 32768
-    assert lay.score_row_bytes == T * split * 4
-    assert lay.stats_offset >= 32 * lay.score_row_bytes
-    assert lay.targets_offset >= lay.stats_offset + 32 * T * 16
+    assert lay.sync_offset == 0 and lay.records_offset >= 256
+    assert lay.stash_offset >= lay.records_offset + 32 * T * 16
+    assert lay.stash_row_bytes == T * split * 4
+    assert lay.targets_offset >= lay.stash_offset + 32 * lay.stash_row_bytes
     assert lay.total_bytes >= lay.targets_offset and lay.total_bytes % 256 == 0
+    for off in (lay.records_offset, lay.stash_offset, lay.targets_offset):
+        assert off % 256 == 0
     assert santa.santa_workspace_size(_shape(), 256, 2) == lay.total_bytes
     # multinomial keeps S sorted targets per head
     lay0 = santa.santa_workspace_layout_query(_shape(), 256, 0)
     assert lay0.total_bytes >= lay0.targets_offset + 32 * 256 * 8
     lay_split = santa.santa_workspace_layout_query(_shape(split_size=128), 256, 2)
     assert lay_split.split_size == 128 and lay_split.num_splits == 256
+
+
+def test_default_split_keeps_splits_per_sequence_bounded(lib):
+    """A sequence has at most 512 splits (one merge wave holds 8 split records per lane);
+    lengths that would need more, or more LDS than a workgroup has, are unsupported."""
+    for n in (1, 1000, 32768, 131072, 200000, 262144, 524288):
+        lay = santa.santa_workspace_layout_query(_shape(max_seq_len=n, kv_stride_seq=n * 8 * 128), 64, 2)
+        assert lay.num_splits <= 512 and lay.num_splits * lay.split_size >= n
+    with pytest.raises(santa.SantaError) as e:
+        santa.santa_workspace_layout_query(_shape(max_seq_len=524289, kv_stride_seq=524289 * 8 * 128), 64, 2)
+    assert e.value.status == UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,S,mode,want", [
@@ -101,7 +115,10 @@ def test_workspace_layout_llama_shape(lib):
     (dict(page_size=16, pages_per_seq=2048, num_pages=2048), 256, 2, OK),
     (dict(kv_stride_tok=1001), 256, 2, INVALID),         # rows not 16-byte aligned
     (dict(kv_stride_tok=0), 256, 2, INVALID),
-    (dict(num_q_heads=64, num_kv_heads=8, split_size=1024), 256, 2, UNSUPPORTED),  # LDS
+    (dict(num_q_heads=64, num_kv_heads=8, split_size=1024), 256, 2, OK),   # 133 KiB of LDS
+    (dict(split_size=64), 256, 2, OK),                  # 512 splits
+    (dict(max_seq_len=40000, split_size=64), 256, 2, UNSUPPORTED),   # 625 splits
+    (dict(max_seq_len=524289), 256, 2, UNSUPPORTED),
 ])
 def test_host_validation(lib, kw, S, mode, want):
     st, _ = _status_of_size(lib, _shape(**kw), S, mode)
@@ -113,6 +130,19 @@ def test_host_validation(lib, kw, S, mode, want):
 def test_null_shape_is_rejected(lib):
     st, _ = _status_of_size(lib, None)
     assert st == INVALID
+    assert lib.santa_decode_path(None, 64, 2) == -INVALID
+
+
+def test_decode_path_rejects_invalid_shapes_before_touching_hip(lib):
+    assert lib.santa_decode_path(ctypes.byref(_shape(head_dim=96)), 64, 2) == -UNSUPPORTED
+    assert lib.santa_decode_path(ctypes.byref(_shape()), 0, 2) == -INVALID
+
+
+def test_workspace_init_validates_before_launch(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.santa_workspace_init(None, 4096, None) == INVALID
+    assert lib.santa_workspace_init(ctypes.c_void_p((1 << 20) + 16), 4096, None) == INVALID
+    assert lib.santa_workspace_init(fake, 255, None) == WS_SMALL
 
 
 def test_decode_rejects_bad_pointers_before_launch(lib):

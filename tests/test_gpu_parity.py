@@ -44,7 +44,7 @@ def test_decode_small_bf16_gqa4(mode, S):
     print(rep)
 
 
-@pytest.mark.parametrize("split", [64, 128, 1024])
+@pytest.mark.parametrize("split", [64, 128, 512, 1024])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_decode_split_sizes(split, mode):
     x = _inputs(lens=(2049, 700, 1))
@@ -108,48 +108,161 @@ def test_indices_deterministic_and_split_invariant():
 
 
 def test_score_pass_intermediates():
-    """Stashed scores and split statistics (§3.2, Pass 1) against the oracle."""
+    """Stashed scores and split records (section 3.2, Pass 1) against the oracle."""
     for G, d, dtype, page in [(4, 128, "bf16", 0), (1, 64, "f32", 0), (7, 128, "bf16", 16)]:
         x = _inputs(G=G, d=d, dtype=dtype, lens=(1000, 1537), page_size=page)
         S, mode = 32, 2
         shape = santa.make_shape(x["q"], x["k"], x["block_table"], max_seq_len=x["workload"].seq_len)
         lay = santa.santa_workspace_layout_query(shape, S, mode)
         B, Hq, _ = x["q"].shape
-        o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
         idx = torch.empty((B, Hq, S), dtype=torch.int32, device="cuda")
         ws = santa.allocate_workspace(shape, S, mode, "cuda")
         santa.santa_score_pass(shape, x["q"], x["k"], x["v"], x["seq_lens"], x["block_table"], S,
                                mode, 0, o, idx, ws)
         torch.cuda.synchronize()
         wsc = ws.cpu()
-        row = lay.score_row_bytes // 4
-        scores = wsc[lay.scores_offset: lay.scores_offset + B * Hq * row * 4].view(torch.float32)
-        scores = scores.view(B, Hq, row).double().numpy()
         T, split = lay.num_splits, lay.split_size
-        stats = wsc[lay.stats_offset: lay.stats_offset + B * Hq * T * 16].view(B, Hq, T, 16)
-        m = stats[..., 0:4].contiguous().view(torch.float32).view(B, Hq, T).double().numpy()
-        l = stats[..., 8:16].contiguous().view(torch.float64).view(B, Hq, T).numpy()
-        assert torch.all(o.cpu() == 0)
+        row = lay.stash_row_bytes // 4
+        stash = wsc[lay.stash_offset: lay.stash_offset + B * Hq * row * 4].view(torch.float32)
+        stash = stash.view(B, Hq, row).double().numpy()
+        rec = wsc[lay.records_offset: lay.records_offset + B * Hq * T * 16].view(torch.int32)
+        rec = rec.view(B, Hq, T, 4)
+        m = rec[..., 0].contiguous().view(torch.float32).double().numpy()
+        l = rec[..., 2].contiguous().view(torch.float32).double().numpy()
+        epoch = rec[..., 1].numpy()
+        assert torch.all(torch.isnan(o.cpu()))      # o is written by the sample pass alone
         w = x["workload"]
         for b in range(B):
             n = int(x["seq_lens"][b])
+            Tb = -(-n // split)
+            assert np.all(epoch[b, :, :Tb] == epoch[0, 0, 0]) and np.all(rec[b, :, :Tb, 3].numpy() == epoch[0, 0, 0])
             for h in range(Hq):
                 kk, _ = H.head_rows(x, b, h // w.group)
                 q = x["q"][b, h].double().cpu().numpy()
                 s_ref = O.scores(q, kk)
                 bound = np.abs(kk * q).sum(1) / math.sqrt(d) * 16 * 2.0 ** -24 + 1e-7
-                err = np.abs(scores[b, h, :n] - s_ref)
+                err = np.abs(stash[b, h, :n] - s_ref)
                 assert np.all(err <= bound), f"score error {err.max():.2e} (b={b}, h={h})"
                 tiles = O.tile_partition(s_ref, split)
-                Tb = -(-n // split)
                 assert np.allclose(m[b, h, :Tb], tiles[:, 0], rtol=0, atol=bound.max())
                 assert np.allclose(l[b, h, :Tb], tiles[:, 1], rtol=2e-5, atol=0)
-                # the tile sums are those of the stashed scores themselves
+                # the statistics are those of the stashed scores themselves
                 for t in range(Tb):
-                    st = scores[b, h, t * split: min(n, (t + 1) * split)]
+                    st = stash[b, h, t * split: min(n, (t + 1) * split)]
                     assert m[b, h, t] == st.max()
                     e = np.exp(st.astype(np.float32) - np.float32(st.max())).astype(np.float64)
                     assert abs(l[b, h, t] / e.sum() - 1) < 1e-6
+        assert santa.workspace_error(ws) == 0
+
+
+def test_fused_and_two_kernel_paths_agree():
+    """santa_decode (one fused kernel here) and score pass + sample pass draw the same indices."""
+    for mode in (0, 1, 2):
+        for lens, page in [((1000, 1537, 64, 17), 0), ((1000, 1537, 333), 16)]:
+            x = _inputs(lens=lens, page_size=page)
+            shape = santa.make_shape(x["q"], x["k"], x["block_table"], max_seq_len=x["workload"].seq_len)
+            assert santa.santa_decode_path(shape, 200, mode) == santa.PATH_FUSED
+            o1, i1, ws1, _ = H.run_hip(x, 200, mode, seed=13)
+            o2, i2, ws2, _ = H.run_hip(x, 200, mode, seed=13, stages="split")
+            assert torch.equal(i1, i2)
+            assert torch.allclose(o1, o2, rtol=1e-5, atol=1e-6)
+            assert santa.workspace_error(ws1) == 0 and santa.workspace_error(ws2) == 0
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """The epoch words let one workspace serve many calls of different shapes in a row,
+    mixing the fused kernel and the two halves."""
+    xa = _inputs(lens=(2049, 700, 1))
+    xb = _inputs(G=1, d=64, dtype="f32", lens=(300, 0, 1500))
+    big = max(santa.santa_workspace_size(santa.make_shape(x["q"], x["k"], None,
+                                                          max_seq_len=x["workload"].seq_len), 128, 0)
+              for x in (xa, xb))
+    ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+    santa.santa_workspace_init(ws)
+    for rep in range(3):
+        for x, mode in ((xa, 2), (xb, 0), (xa, 1), (xb, 2)):
+            shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len)
+            B, Hq, d = x["q"].shape
+            o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+            idx = torch.empty((B, Hq, 128), dtype=torch.int32, device="cuda")
+            args = (shape, x["q"], x["k"], x["v"], x["seq_lens"], None, 128, mode, 40 + rep, o, idx, ws)
+            if rep == 1:
+                santa.santa_score_pass(*args)
+                santa.santa_sample_pass(*args)
+            else:
+                santa.santa_decode(*args)
+            torch.cuda.synchronize()
+            H.check_all(x, 128, mode, 40 + rep, o.cpu(), idx.cpu())
+    assert santa.workspace_error(ws) == 0
+    # between calls the whole workspace is zero except the epoch word, which
+    # counts the calls that published records (one per decode or score pass)
+    words = ws.view(torch.int32).cpu()
+    assert int(words[0]) == 12 and int(words[1]) == 0
+    assert torch.count_nonzero(words[2:]) == 0
+
+
+def test_sample_pass_without_score_pass_sets_error():
+    """A sample pass whose records no score pass wrote flags the error word at once
+    (no wait) and leaves the workspace usable after santa_workspace_init."""
+    x = _inputs(lens=(1000, 1537, 64))
+    S, mode = 64, 1
+    shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len)
+    B, Hq, d = x["q"].shape
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, Hq, S), dtype=torch.int32, device="cuda")
+    ws = santa.allocate_workspace(shape, S, mode, "cuda")
+    args = (shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, 5, o, idx, ws)
+    santa.santa_sample_pass(*args)                 # fresh workspace: epoch 0
+    torch.cuda.synchronize()
+    assert santa.workspace_error(ws) != 0
+    santa.santa_workspace_init(ws)
+    santa.santa_score_pass(*args)
+    santa.santa_sample_pass(*args)
+    torch.cuda.synchronize()
+    assert santa.workspace_error(ws) == 0
+    H.check_all(x, S, mode, 5, o.cpu(), idx.cpu())
+    santa.santa_sample_pass(*args)                 # records already consumed
+    torch.cuda.synchronize()
+    assert santa.workspace_error(ws) != 0
+    santa.santa_workspace_init(ws)
+    santa.santa_decode(*args)
+    torch.cuda.synchronize()
+    assert santa.workspace_error(ws) == 0
+    H.check_all(x, S, mode, 5, o.cpu(), idx.cpu())
+
+
+def test_graph_replays_match_eager():
+    """A captured decode call replays with the same indices (inputs rewritten between replays)."""
+    x = _inputs(lens=(1000, 1537, 64, 17))
+    S, mode = 128, 2
+    shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len)
+    B, Hq, d = x["q"].shape
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, Hq, S), dtype=torch.int32, device="cuda")
+    ws = santa.allocate_workspace(shape, S, mode, "cuda")
+    q_in = x["q"].clone()
+    args = (shape, q_in, x["k"], x["v"], x["seq_lens"], None, S, mode, 77, o, idx, ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        santa.santa_decode(*args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        santa.santa_decode(*args)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        q_in.copy_(x["q"] * (1.0 + 0.25 * rep))
+        graph.replay()
+        torch.cuda.synchronize()
+        o_g, i_g = o.cpu().clone(), idx.cpu().clone()
+        santa.santa_decode(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(i_g, idx.cpu()), rep
+        assert torch.allclose(o_g, o.cpu(), rtol=1e-5, atol=1e-6), rep
+    assert santa.workspace_error(ws) == 0
 
 
 def test_toy_unbiased_over_4096_seeds():
