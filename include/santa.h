@@ -41,8 +41,8 @@
  *
  * State: the library keeps none between calls on the host.  A workspace must
  * be all zero before its first call (santa_workspace_init, or any zero fill).
- * Every completed call leaves it all zero again except for the epoch word at
- * byte 0 (and the error word at byte 4 after a failed wait), so one workspace
+ * Every completed call leaves it all zero again (except for the error word at
+ * byte 0 after a failed wait), so one workspace
  * large enough for each of them serves calls of any shapes, modes and sample
  * counts in any order.  The two-kernel path counts as one call from the start
  * of santa_score_pass to the end of the santa_sample_pass that follows it.
@@ -113,28 +113,27 @@ typedef struct santa_shape {
 
 /*
  * Workspace layout (byte offsets into the caller's workspace, 256-byte aligned):
- *   sync     synchronisation words (barrier_offset bytes at the start): the
- *            epoch of the last call that published split records (byte 0),
- *            a 32-bit error word (byte 4) that becomes nonzero if a bounded
- *            wait of a call gave up (that call's outputs are invalid;
- *            santa_workspace_init clears it), and per-call arrival counters;
+ *   sync     barrier_offset bytes at the start: a 32-bit error word (byte 0)
+ *            that becomes nonzero if a bounded wait of a call gave up (that
+ *            call's outputs are invalid; santa_workspace_init clears it);
  *   barrier  [B, Hkv] x 18 lines of 128 bytes: per (sequence, KV head) the
  *            counts of its splits that have published their records and that
  *            have added their output in the current call, and 16 copies of a
- *            flag raised to the call's epoch once all of them published;
+ *            flag raised once all of them published;
  *   accum    fp32 [B, Hkv, 16, G, d]: partial outputs, added by the splits of a
  *            (sequence, KV head) into slot (split % 16) and summed into o by
  *            the last of them;
- *   records  [B, Hq, num_splits] x 16 bytes: per split the maximum score m and
+ *   records  [B, Hq, num_splits] x 8 bytes: per split the maximum score m and
  *            l = sum exp(s_i - m) (the tile partition functions of section 3.2,
- *            Pass 1), each in a 64-bit word tagged with the call's epoch;
+ *            Pass 1) as one word, fp32 l in the high and fp32 m in the low half
+ *            (l >= 1 for a split with keys, so 0 means not written yet);
  *   stash    fp32 [B, Hq, num_splits * split_size]: scaled scores s_i (the
  *            "score stash" of section 3.2, Pass 1), written by
  *            santa_score_pass and read (and cleared) by santa_sample_pass; row
  *            b*Hq+h starts at stash_offset + (b*Hq+h) * stash_row_bytes;
  *   targets  fp64 [B, Hq, S]: sorted multinomial targets (mode 0 only, else
  *            empty).
- * All of it except the epoch and error words is zero between calls.
+ * All of it except the error word is zero between calls.
  */
 typedef struct santa_workspace_layout {
     size_t total_bytes;

@@ -170,7 +170,7 @@ def allocate_workspace(shape: Shape, num_samples: int, mode: int, device) -> tor
 def workspace_error(workspace: torch.Tensor) -> int:
     """The workspace's error word (nonzero: a bounded wait of a decode call gave up).
     Reads device memory: synchronises with the current stream."""
-    return int(workspace[4:8].view(torch.int32).item())
+    return int(workspace[0:4].view(torch.int32).item())
 
 
 def _ptr(t: Optional[torch.Tensor]):

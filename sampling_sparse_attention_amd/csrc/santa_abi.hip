@@ -113,7 +113,7 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     L.accum_offset = align256(L.barrier_offset + (size_t)s->batch * s->num_kv_heads * santa::kBarrierStride * 4);
     L.records_offset = align256(L.accum_offset + (size_t)s->batch * s->num_q_heads * santa::kOutSlots *
                                                      s->head_dim * sizeof(float));
-    L.stash_offset = align256(L.records_offset + rows * (size_t)T * 16);
+    L.stash_offset = align256(L.records_offset + rows * (size_t)T * 8);
     L.stash_row_bytes = (size_t)T * split * sizeof(float);
     L.targets_offset = align256(L.stash_offset + rows * L.stash_row_bytes);
     const size_t targets = mode == SANTA_MODE_MULTINOMIAL ? rows * (size_t)S * sizeof(double) : 0;

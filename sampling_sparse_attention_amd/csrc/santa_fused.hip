@@ -13,7 +13,7 @@
 namespace santa {
 
 template <int G, int D, typename E, int NT>
-__device__ __forceinline__ void fused_item(const Params& p, const Item& it, uint32_t epoch,
+__device__ __forceinline__ void fused_item(const Params& p, const Item& it, const uint4 (&qf)[G],
                                            unsigned char* smem) {
     if (it.n == 0) {
         if (it.t == 0) write_empty<G, D, NT>(p, it);
@@ -27,15 +27,15 @@ __device__ __forceinline__ void fused_item(const Params& p, const Item& it, uint
 
     load_pages<NT>(p, it, pages);
     __syncthreads();
-    stream_scores<G, D, E, NT>(p, it, sc, pages);
+    stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
     __syncthreads();
     split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     __syncthreads();
-    // a reader re-reads a record until its epoch matches, so the barrier need
-    // not wait for these stores to complete
-    publish_stats<G>(p, it, hs, epoch);
-    group_barrier(p, it, epoch, [&] { systematic_offsets<G, 1>(p, it, hs); });
-    prefix_and_sample<G, D, E, NT>(p, it, L, smem, epoch, kSpinLimit);
+    // a reader re-reads a record until it is written, so the barrier need not
+    // wait for these stores to complete
+    publish_stats<G>(p, it, hs);
+    group_barrier(p, it, [&] { systematic_offsets<G, 1>(p, it, hs); });
+    prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit);
     finish_output<G, D, NT>(p, it);
 }
 
@@ -45,11 +45,10 @@ template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
 void fused_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const uint32_t epoch = next_epoch(read_epoch(p));
-    unsigned int prev = 0;
-    if (threadIdx.x == 0) prev = arrive(p);
-    fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), epoch, smem);
-    if (threadIdx.x == 0) finish_arrival(p, prev, epoch);
+    const Item at = item_coords(p, blockIdx.x);
+    uint4 qf[G];
+    load_q<G, D, E, NT>(p, at.b, at.g, qf);
+    fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), qf, smem);
 }
 
 template <int G, int D, typename E>

@@ -15,24 +15,14 @@ constexpr int kMaxSortSamples = 8192;
 constexpr int kTargetChunk = 256;        // targets per merge-path pass of one wave
 constexpr int kSpinLimit = 1 << 21;      // polls of a bounded wait (about 1 us each)
 
-// Workspace synchronisation words (first kSyncBytes bytes of the workspace),
-// zero before the first call and left valid by every completed call.
-//   epoch:  epoch of the last call that published split records; a call that
-//           publishes uses epoch + 1 and stores it here once every one of its
-//           workgroups has read the old value;
-//   error:  nonzero once a bounded wait gave up (outputs of that call invalid);
-//   done:   arrival slots that have seen all of their workgroups this call;
-//   arrive: per-slot counts of workgroups that have read the epoch this call
-//           (workgroup w uses slot w % kArriveSlots; one 128-byte line per
-//           slot, so the counting atomics never queue on one address).
-constexpr int kArriveSlots = 64;
-constexpr int kArriveStride = 32;        // 32-bit words between slots
+// Workspace state word (first kSyncBytes bytes of the workspace): the error
+// word, nonzero once a bounded wait gave up (the outputs of that call are
+// invalid and the workspace needs santa_workspace_init).  Every other byte of
+// the workspace is zero between calls: a record or flag that is nonzero was
+// written by the current call.
 struct SyncWords {
-    unsigned int epoch;
     unsigned int error;
-    unsigned int done;
-    unsigned int pad[kArriveStride - 3];
-    unsigned int arrive[kArriveSlots * kArriveStride];
+    unsigned int pad[63];
 };
 constexpr size_t kSyncBytes = sizeof(SyncWords);
 
@@ -42,8 +32,8 @@ constexpr size_t kSyncBytes = sizeof(SyncWords);
 //                  last one resets it);
 //   line 1 word 0: splits that have added their output this call (the last one
 //                  finishes the output and clears the group's state);
-//   lines 2 .. 1+kFlagCopies: copies of a flag raised to the call's epoch once
-//                  all splits published (a waiting workgroup polls copy
+//   lines 2 .. 1+kFlagCopies: copies of a flag raised to 1 once all splits
+//                  published (a waiting workgroup polls copy
 //                  blockIdx % kFlagCopies, so no line is polled by many).
 constexpr int kFlagCopies = 16;
 constexpr int kBarrierLines = 2 + kFlagCopies;
@@ -63,8 +53,8 @@ struct Params {
     float* o;
     int32_t* idx;
     SyncWords* sync;
-    unsigned long long* records;  // [B, Hq, T] x 2 words: (epoch << 32 | m bits), (epoch << 32 | l bits)
-    unsigned int* barrier;        // [B * Hkv] x kBarrierStride words: counts, epoch flags
+    unsigned long long* records;  // [B, Hq, T] words: l bits << 32 | m bits (0: not written yet)
+    unsigned int* barrier;        // [B * Hkv] x kBarrierStride words: counts, flags
     float* accum;                 // [B * Hkv][kOutSlots][G * D] partial outputs (zero between calls)
     float* stash;                 // [B, Hq, T * split] scaled scores (two-kernel path)
     double* targets;              // [B, Hq, S] sorted uniforms (multinomial only)

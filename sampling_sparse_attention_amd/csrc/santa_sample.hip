@@ -11,11 +11,6 @@ namespace santa {
 template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) void sample_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const uint32_t epoch = read_epoch(p);     // the epoch its score pass published
-    if (epoch == 0) {                          // no score pass ever ran on this workspace
-        if (threadIdx.x == 0) __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
     const Item it = make_item(p, blockIdx.x);
     if (it.n == 0) {
         if (it.t == 0) write_empty<G, D, NT>(p, it);
@@ -44,7 +39,7 @@ __global__ __launch_bounds__(NT) void sample_kernel(Params p) {
     __syncthreads();
     // the records come from the score pass, an earlier launch: one missing now
     // means no score pass preceded this one, which is an error, not a wait
-    prefix_and_sample<G, D, E, NT>(p, it, L, smem, epoch, 0);
+    prefix_and_sample<G, D, E, NT>(p, it, L, smem, 0);
     finish_output<G, D, NT>(p, it);
 }
 

@@ -17,9 +17,9 @@ size_t sort_lds_bytes(int S) {
 template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) void score_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const uint32_t epoch = next_epoch(read_epoch(p));
-    unsigned int prev = 0;
-    if (threadIdx.x == 0) prev = arrive(p);
+    const Item at = item_coords(p, blockIdx.x);
+    uint4 qf[G];
+    load_q<G, D, E, NT>(p, at.b, at.g, qf);
     const Item it = make_item(p, blockIdx.x);
     if (it.ns != 0) {
         const LdsLayout L = lds_layout(G, D, p.split, NT);
@@ -28,11 +28,11 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
         HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
         load_pages<NT>(p, it, pages);
         __syncthreads();
-        stream_scores<G, D, E, NT>(p, it, sc, pages);
+        stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
         __syncthreads();
         split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
         __syncthreads();
-        publish_stats<G>(p, it, hs, epoch);
+        publish_stats<G>(p, it, hs);
         // the stash: scaled scores of the split, coalesced 16-byte stores
         constexpr int NW = NT / 64;
         const int lane = threadIdx.x & 63;
@@ -48,7 +48,6 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
             }
         }
     }
-    if (threadIdx.x == 0) finish_arrival(p, prev, epoch);
 }
 
 // Multinomial targets: the S uniforms of every (sequence, query head), sorted

@@ -35,12 +35,17 @@ struct Item {
     int Tb;        // splits of sequence b
 };
 
-__device__ __forceinline__ Item make_item(const Params& p, int item) {
+__device__ __forceinline__ Item item_coords(const Params& p, int item) {
     Item it;
     it.t = item % p.T;
     const int grp = item / p.T;
     it.g = grp % p.Hkv;
     it.b = grp / p.Hkv;
+    return it;
+}
+
+__device__ __forceinline__ Item make_item(const Params& p, int item) {
+    Item it = item_coords(p, item);
     it.n = seq_len_of(p, it.b);
     it.key0 = it.t * p.split;
     it.ns = max(0, min(p.split, it.n - it.key0));
@@ -132,55 +137,47 @@ __device__ __forceinline__ int64_t row_offset(const Params& p, const Item& it, i
 // loads per lane.  A wave issues the loads of CB chunks (16 loads per lane)
 // before using any of them.  Each lane forms R*G partial dot products; a
 // reduce-scatter across the row's lanes leaves every lane owning whole scores.
+//
+// The loads carry no branches (a row past the split re-reads the split's first
+// row), and the first batch is straight-line code after the q loads, so the
+// compiler waits for q and then for each chunk in turn instead of for every
+// load before the first K load is even issued.
 // ---------------------------------------------------------------------------
 template <int G, int D, typename E, int NT>
-__device__ __forceinline__ void stream_scores(const Params& p, const Item& it, float* sc,
-                                              const int* pages) {
-    constexpr int NW = NT / 64;
-    constexpr int LPR = D * E::bytes / 16;
-    constexpr int RPL = 64 / LPR;
-    constexpr int R = 16 / RPL;
-    constexpr int CB = (16 / R) > 0 ? 16 / R : 1;
-    constexpr int NV = R * G;
-    constexpr int NVP = (NV + LPR - 1) / LPR * LPR;
-    constexpr int M = NVP / LPR;
+struct ScoreStream {
+    static constexpr int NW = NT / 64;
+    static constexpr int LPR = D * E::bytes / 16;
+    static constexpr int RPL = 64 / LPR;
+    static constexpr int R = 16 / RPL;
+    static constexpr int CB = (16 / R) > 0 ? 16 / R : 1;
+    static constexpr int NV = R * G;
+    static constexpr int NVP = (NV + LPR - 1) / LPR * LPR;
+    static constexpr int M = NVP / LPR;
     static_assert(LPR >= 2 && LPR <= 32 && 16 % RPL == 0, "row shape");
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int c = lane / LPR;
-    const int li = lane % LPR;
-    const int split = p.split;
-
-    uint4 qf[G];
-    {
-        const char* qb = reinterpret_cast<const char*>(p.q) +
-                         (((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D) * E::bytes + li * 16;
-#pragma unroll
-        for (int h = 0; h < G; ++h) qf[h] = load16(qb + (int64_t)h * D * E::bytes);
-    }
-    const char* kbase = reinterpret_cast<const char*>(p.k);
-    const int nchunks = (it.ns + 15) >> 4;
-
-    for (int base = wave; base < nchunks; base += NW * CB) {
-        uint4 kd[CB][R];
+    // Loads of the CB chunks base, base + NW, ... (16 rows each).
+    __device__ __forceinline__ static void issue(const Params& p, const Item& it, const int* pages,
+                                                 const char* kbase, int64_t first, int base, int nchunks,
+                                                 int c, int li, uint4 (&kd)[CB][R]) {
 #pragma unroll
         for (int k = 0; k < CB; ++k) {
             const int ch = base + k * NW;
             const int r0 = ch << 4;
             // a 16-row chunk never straddles a page (pages >= 16 rows, r0 % 16 == 0)
-            const int64_t off = (ch < nchunks) ? row_offset(p, it, r0, pages) : 0;
+            const int64_t off = (ch < nchunks) ? row_offset(p, it, r0, pages) : first;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int rr = r * RPL + c;
-                if (ch < nchunks && r0 + rr < it.ns) {
-                    kd[k][r] = load16(kbase + (off + (int64_t)rr * p.stride_tok) * E::bytes + li * 16);
-                } else {
-                    kd[k][r] = make_uint4(0u, 0u, 0u, 0u);
-                }
+                const bool ok = ch < nchunks && r0 + rr < it.ns;
+                const int64_t o = ok ? off + (int64_t)rr * p.stride_tok : first;
+                kd[k][r] = load16(kbase + o * E::bytes + li * 16);
             }
         }
+    }
 
+    __device__ __forceinline__ static void score(const Params& p, const Item& it, float* sc, int base,
+                                                 int nchunks, int c, int li, const uint4 (&qf)[G],
+                                                 const uint4 (&kd)[CB][R]) {
 #pragma unroll
         for (int k = 0; k < CB; ++k) {
             const int ch = base + k * NW;
@@ -200,11 +197,45 @@ __device__ __forceinline__ void stream_scores(const Params& p, const Item& it, f
                         const int r = vi / G;
                         const int h = vi - r * G;
                         const int local = (ch << 4) + r * RPL + c;
-                        if (local < it.ns) sc[h * split + local] = acc[j] * p.scale;
+                        if (local < it.ns) sc[h * p.split + local] = acc[j] * p.scale;
                     }
                 }
             }
         }
+    }
+};
+
+// This lane's 16-byte pieces of the G query rows of KV head g of sequence b
+// (the piece li = lane % LPR of each row, as stream_scores consumes them).
+// Issued at the start of a workgroup, before the sequence length is known, so
+// that both loads share one memory round trip.
+template <int G, int D, typename E, int NT>
+__device__ __forceinline__ void load_q(const Params& p, int b, int g, uint4 (&qf)[G]) {
+    const int li = (threadIdx.x & 63) % ScoreStream<G, D, E, NT>::LPR;
+    const char* qb = reinterpret_cast<const char*>(p.q) + (((int64_t)b * p.Hq + (int64_t)g * G) * D) * E::bytes +
+                     li * 16;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qf[h] = load16(qb + (int64_t)h * D * E::bytes);
+}
+
+template <int G, int D, typename E, int NT>
+__device__ __forceinline__ void stream_scores(const Params& p, const Item& it, float* sc,
+                                              const int* pages, const uint4 (&qf)[G]) {
+    using SS = ScoreStream<G, D, E, NT>;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int c = lane / SS::LPR;
+    const int li = lane % SS::LPR;
+    const char* kbase = reinterpret_cast<const char*>(p.k);
+    const int nchunks = (it.ns + 15) >> 4;
+    const int64_t first = row_offset(p, it, 0, pages);
+
+    uint4 kd[SS::CB][SS::R];
+    SS::issue(p, it, pages, kbase, first, wave, nchunks, c, li, kd);
+    SS::score(p, it, sc, wave, nchunks, c, li, qf, kd);
+    for (int base = wave + SS::NW * SS::CB; base < nchunks; base += SS::NW * SS::CB) {
+        SS::issue(p, it, pages, kbase, first, base, nchunks, c, li, kd);
+        SS::score(p, it, sc, base, nchunks, c, li, qf, kd);
     }
 }
 
@@ -265,37 +296,36 @@ __device__ __forceinline__ void systematic_offsets(const Params& p, const Item& 
     }
 }
 
-// Record of split t of query head hq of sequence b: two 64-bit words, each
-// (epoch << 32 | 32 payload bits), written and read as single atomic words.
+// Record of split t of query head hq of sequence b: one 64-bit word
+// (l_t bits << 32 | m_t bits), written and read as a single atomic word.  A
+// split with keys has l_t >= 1 (its maximum contributes exp(0)), so a record
+// is written exactly when its high half is nonzero; records are zero between
+// calls.
 __device__ __forceinline__ unsigned long long* record_of(const Params& p, int b, int hq, int t) {
-    return p.records + (((int64_t)b * p.Hq + hq) * p.T + t) * 2;
+    return p.records + ((int64_t)b * p.Hq + hq) * p.T + t;
 }
 
 template <int G>
-__device__ __forceinline__ void publish_stats(const Params& p, const Item& it, const HeadState* hs,
-                                              uint32_t epoch) {
+__device__ __forceinline__ void publish_stats(const Params& p, const Item& it, const HeadState* hs) {
     const int h = threadIdx.x;
     if (h < G) {
-        unsigned long long* rec = record_of(p, it.b, it.g * G + h, it.t);
-        const unsigned long long tag = (unsigned long long)epoch << 32;
-        __hip_atomic_store(rec, tag | __float_as_uint(hs[h].m_t), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(rec + 1, tag | __float_as_uint(hs[h].l_t), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long r =
+            (unsigned long long)__float_as_uint(hs[h].l_t) << 32 | __float_as_uint(hs[h].m_t);
+        __hip_atomic_store(record_of(p, it.b, it.g * G + h, it.t), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Barrier of the Tb splits of one (sequence, KV head) in the fused kernel: a
-// sense-reversing counter.  Each split counts itself in once its records are
-// written; the last one resets the count and raises the flag to this call's
-// epoch; the others poll the flag word alone, so waiting adds almost no
-// memory traffic.  `overlap()` runs on every thread meanwhile (thread 0 after
-// its wait).  Returns false if the bounded wait gave up.
+// Barrier of the Tb splits of one (sequence, KV head) in the fused kernel.
+// Each split counts itself in once its records are written; the last one
+// resets the count and raises the 16 flag copies; the others poll one copy
+// each, so waiting adds almost no memory traffic.  The flags are cleared by
+// the group's last split at the end of the call (finish_output).  `overlap()`
+// runs on every thread meanwhile (thread 0 after its wait).  Returns false if
+// the bounded wait gave up.
 // ---------------------------------------------------------------------------
 template <typename Overlap>
-__device__ __forceinline__ bool group_barrier(const Params& p, const Item& it, uint32_t epoch,
-                                              Overlap&& overlap) {
+__device__ __forceinline__ bool group_barrier(const Params& p, const Item& it, Overlap&& overlap) {
     __shared__ int s_ok;
     if (threadIdx.x == 0) {
         unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
@@ -304,11 +334,11 @@ __device__ __forceinline__ bool group_barrier(const Params& p, const Item& it, u
         if (prev == (unsigned int)it.Tb - 1u) {
             __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int c = 0; c < kFlagCopies; ++c)
-                __hip_atomic_store(bar + 32 * (2 + c), epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(bar + 32 * (2 + c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             const unsigned int* flag = bar + 32 * (2 + blockIdx.x % kFlagCopies);
             for (int iter = 0;
-                 __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch; ++iter) {
+                 __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++iter) {
                 if (iter >= kSpinLimit) {
                     ok = 0;
                     __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -612,7 +642,7 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
 // ---------------------------------------------------------------------------
 template <int G, int D, typename E, int NT>
 __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
-                                                  unsigned char* smem, uint32_t epoch, int spin_limit) {
+                                                  unsigned char* smem, int spin_limit) {
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
@@ -626,8 +656,8 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
         float mr[kRecPerLane], lr[kRecPerLane];
         // first an ordinary (cached) read: after the barrier every record is
         // normally in place, and the splits' workgroups on one XCD then share
-        // its L2 copy; a record whose epoch does not match yet is re-read
-        // below with device-coherent loads until it does
+        // its L2 copy; a record not written yet is re-read below with
+        // device-coherent loads until it is
         bool fresh = true;
 #pragma unroll
         for (int k = 0; k < kRecPerLane; ++k) {
@@ -635,10 +665,10 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
             mr[k] = -INFINITY;
             lr[k] = 0.0f;
             if (k < K && j < Tb) {
-                const ulonglong2 r = *reinterpret_cast<const ulonglong2*>(rec + 2 * j);
-                fresh &= (uint32_t)(r.x >> 32) == epoch && (uint32_t)(r.y >> 32) == epoch;
-                mr[k] = __uint_as_float((uint32_t)r.x);
-                lr[k] = __uint_as_float((uint32_t)r.y);
+                const unsigned long long r = rec[j];
+                fresh &= (r >> 32) != 0;
+                mr[k] = __uint_as_float((uint32_t)r);
+                lr[k] = __uint_as_float((uint32_t)(r >> 32));
             }
         }
         for (int iter = 0; !__all(fresh); ++iter) {
@@ -649,13 +679,11 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
                 mr[k] = -INFINITY;
                 lr[k] = 0.0f;
                 if (k < K && j < Tb) {
-                    const unsigned long long a =
-                        __hip_atomic_load(rec + 2 * j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const unsigned long long w =
-                        __hip_atomic_load(rec + 2 * j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok &= (uint32_t)(a >> 32) == epoch && (uint32_t)(w >> 32) == epoch;
-                    mr[k] = __uint_as_float((uint32_t)a);
-                    lr[k] = __uint_as_float((uint32_t)w);
+                    const unsigned long long r =
+                        __hip_atomic_load(rec + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok &= (r >> 32) != 0;
+                    mr[k] = __uint_as_float((uint32_t)r);
+                    lr[k] = __uint_as_float((uint32_t)(r >> 32));
                 }
             }
             if (__all(ok)) break;
@@ -731,7 +759,7 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // counts itself done.  The last one -- every other split of the group has then
 // passed the barrier and read the records and targets -- sums the kOutSlots
 // slots, stores o = (1/S) * sum (Eq. 3) for the G heads, and returns to zero
-// the slots, the epoch flags, the group's split records and (multinomial) its
+// the slots, the barrier flags, the group's split records and (multinomial) its
 // targets, so that a completed call leaves this state all zero.
 // ---------------------------------------------------------------------------
 template <int G, int D, int NT>
@@ -773,9 +801,8 @@ __device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
         __hip_atomic_store(bar + 32 * (2 + threadIdx.x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int i = threadIdx.x; i < G * it.Tb; i += NT) {
         const int h = i / it.Tb;
-        unsigned long long* r = record_of(p, it.b, it.g * G + h, i - h * it.Tb);
-        __hip_atomic_store(r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(r + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(record_of(p, it.b, it.g * G + h, i - h * it.Tb), 0ull, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     if (p.mode == 0) {
         double* tg = p.targets + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
@@ -790,48 +817,6 @@ __device__ __forceinline__ void write_empty(const Params& p, const Item& it) {
     for (int i = threadIdx.x; i < G * D; i += NT) o[i] = 0.0f;
     int32_t* idx = p.idx + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
     for (int i = threadIdx.x; i < G * p.S; i += NT) idx[i] = -1;
-}
-
-// ---------------------------------------------------------------------------
-// Call epochs.  Every workgroup reads the epoch word once (an uncontended
-// atomic load).  A call that publishes split records uses epoch + 1 and counts
-// its workgroups in: the last of each arrival slot clears the slot and counts
-// the slot done, the last slot stores the new epoch.  The sample pass of the
-// two-kernel path reads the epoch its score pass stored and does not advance.
-// ---------------------------------------------------------------------------
-// The epoch a publishing call uses after `e`; never 0, which marks a record or
-// flag as not written.
-__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1u == 0u ? 1u : e + 1u; }
-
-__device__ __forceinline__ uint32_t read_epoch(const Params& p) {
-    __shared__ uint32_t s_epoch;
-    if (threadIdx.x == 0)
-        s_epoch = __hip_atomic_load(&p.sync->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    return s_epoch;
-}
-
-// Thread 0 only: this workgroup's arrival; returns the count before it.
-__device__ __forceinline__ unsigned int arrive(const Params& p) {
-    const int k = blockIdx.x % kArriveSlots;
-    return __hip_atomic_fetch_add(&p.sync->arrive[k * kArriveStride], 1u, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Thread 0 only, with the value arrive() returned: the last workgroup of the
-// last slot publishes `epoch` for the next call.
-__device__ __forceinline__ void finish_arrival(const Params& p, unsigned int prev, uint32_t epoch) {
-    const unsigned int k = blockIdx.x % kArriveSlots;
-    const unsigned int slot_size = (gridDim.x - k + kArriveSlots - 1) / kArriveSlots;
-    if (prev != slot_size - 1) return;
-    __hip_atomic_store(&p.sync->arrive[k * kArriveStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned int slots = gridDim.x < (unsigned)kArriveSlots ? gridDim.x : (unsigned)kArriveSlots;
-    const unsigned int d = __hip_atomic_fetch_add(&p.sync->done, 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
-    if (d == slots - 1) {
-        __hip_atomic_store(&p.sync->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.sync->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 }  // namespace santa

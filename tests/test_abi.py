@@ -68,7 +68,7 @@ def test_workspace_layout_llama_shape(lib):
     T, split = lay.num_splits, lay.split_size
     assert split % 64 == 0 and T * split >= 32768 and (T - 1) * split < 32768
     assert lay.sync_offset == 0 and lay.records_offset >= 256
-    assert lay.stash_offset >= lay.records_offset + 32 * T * 16
+    assert lay.stash_offset >= lay.records_offset + 32 * T * 8
     assert lay.stash_row_bytes == T * split * 4
     assert lay.targets_offset >= lay.stash_offset + 32 * lay.stash_row_bytes
     assert lay.total_bytes >= lay.targets_offset and lay.total_bytes % 256 == 0
