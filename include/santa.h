@@ -105,7 +105,7 @@ typedef struct santa_shape {
     int32_t num_pages;        /* paged: pages in each cache; table entries are clamped to [0, num_pages) */
     int32_t dtype;            /* SANTA_DTYPE_* of q, K and V */
     int32_t split_size;       /* keys per split of the score pass: 0 (library default) or a
-                                 multiple of 64 in [64, 1024] */
+                                 power of two in [64, 1024] */
     int64_t kv_stride_seq;    /* elements between sequences (contiguous) or pages (paged) */
     int64_t kv_stride_tok;    /* elements between consecutive tokens */
     int64_t kv_stride_head;   /* elements between KV heads */

@@ -86,8 +86,8 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     int split = s->split_size;
     if (split == 0) {
         split = default_split(*s, G);
-    } else if (split < 64 || split > santa::kMaxSplit || split % 64) {
-        return fail(SANTA_STATUS_INVALID_ARGUMENT, "split_size %d is not a multiple of 64 in [64, %d]",
+    } else if (split < 64 || split > santa::kMaxSplit || (split & (split - 1))) {
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "split_size %d is not a power of two in [64, %d]",
                     split, santa::kMaxSplit);
     }
     if (!split_fits(G, s->head_dim, split))

@@ -229,16 +229,14 @@ struct Bf16 {
                                               __builtin_bit_cast(bf16x2_t, q.w), acc, false);
         return acc;
     }
-    // EL (1 or 2) consecutive elements of a V row, widened exactly to fp32
-    template <int EL>
-    __device__ static __forceinline__ void load_row_part(const void* p, float* out) {
-        if constexpr (EL == 2) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-            out[0] = __uint_as_float(w << 16);
-            out[1] = __uint_as_float(w & 0xFFFF0000u);
-        } else {
-            const uint16_t w = *reinterpret_cast<const uint16_t*>(p);
-            out[0] = __uint_as_float((uint32_t)w << 16);
+    // acc[e] += w * x_e for the 8 bf16 of a 16-byte piece of a V row (exact
+    // widening to fp32, element e at bits 16e of the piece)
+    __device__ static __forceinline__ void axpy16(float w, const uint4& x, float* acc) {
+        const uint32_t v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(w, __uint_as_float(v[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(w, __uint_as_float(v[i] & 0xFFFF0000u), acc[2 * i + 1]);
         }
     }
 };
@@ -252,15 +250,11 @@ struct F32 {
         acc = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), acc);
         return acc;
     }
-    template <int EL>
-    __device__ static __forceinline__ void load_row_part(const void* p, float* out) {
-        if constexpr (EL == 2) {
-            const float2 w = *reinterpret_cast<const float2*>(p);
-            out[0] = w.x;
-            out[1] = w.y;
-        } else {
-            out[0] = *reinterpret_cast<const float*>(p);
-        }
+    __device__ static __forceinline__ void axpy16(float w, const uint4& x, float* acc) {
+        acc[0] = fmaf(w, __uint_as_float(x.x), acc[0]);
+        acc[1] = fmaf(w, __uint_as_float(x.y), acc[1]);
+        acc[2] = fmaf(w, __uint_as_float(x.z), acc[2]);
+        acc[3] = fmaf(w, __uint_as_float(x.w), acc[3]);
     }
 };
 

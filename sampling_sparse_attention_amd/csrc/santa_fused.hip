@@ -29,14 +29,13 @@ __device__ __forceinline__ void fused_item(const Params& p, const Item& it, cons
     __syncthreads();
     stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
     __syncthreads();
-    split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
-    __syncthreads();
-    // a reader re-reads a record until it is written, so the barrier need not
-    // wait for these stores to complete
-    publish_stats<G>(p, it, hs);
+    // each head's wave publishes its record; a reader re-reads a record until it
+    // is written, so neither a workgroup barrier nor the stores' completion is
+    // needed before the count at the group barrier
+    split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     group_barrier(p, it, [&] { systematic_offsets<G, 1>(p, it, hs); });
     prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit);
-    finish_output<G, D, NT>(p, it);
+    finish_output<G, D, NT>(p, it, L, smem);
 }
 
 // Four waves per SIMD (all 1024 splits of a batch-1, 8-KV-head, 32k-token

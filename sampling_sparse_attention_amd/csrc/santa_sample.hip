@@ -34,13 +34,13 @@ __global__ __launch_bounds__(NT) void sample_kernel(Params p) {
         }
     }
     __syncthreads();
-    split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
+    split_stats<G, NT, false>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     systematic_offsets<G, 0>(p, it, hs);
     __syncthreads();
     // the records come from the score pass, an earlier launch: one missing now
     // means no score pass preceded this one, which is an error, not a wait
     prefix_and_sample<G, D, E, NT>(p, it, L, smem, 0);
-    finish_output<G, D, NT>(p, it);
+    finish_output<G, D, NT>(p, it, L, smem);
 }
 
 template <int G, int D, typename E>

@@ -30,9 +30,8 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
         __syncthreads();
         stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
         __syncthreads();
-        split_stats<G, NT>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
+        split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
         __syncthreads();
-        publish_stats<G>(p, it, hs);
         // the stash: scaled scores of the split, coalesced 16-byte stores
         constexpr int NW = NT / 64;
         const int lane = threadIdx.x & 63;

@@ -8,8 +8,9 @@
 //                  section 2, Eq. 1; section 3.2, Pass 1);
 //   split_stats    per head: the split's maximum m_t, the fixed-point masses
 //                  e_i = exp(s_i - m_t), their in-split prefix P_i and total
-//                  l_t (the tile partition function of section 3.2, Pass 1);
-//   publish_stats  writes (m_t, l_t) for the other workgroups of the sequence;
+//                  l_t (the tile partition function of section 3.2, Pass 1),
+//                  and the record (m_t, l_t) for the other workgroups of the
+//                  sequence;
 //   group_barrier  waits until every split of the sequence has published;
 //   prefix_and_sample
 //                  per head (one wave): merges the splits' statistics to a
@@ -74,13 +75,14 @@ struct LdsLayout {
     uint32_t prefix;    // u64 [G][split] in-split inclusive prefix of fixed-point masses
     uint32_t pages;     // int [split/16 + 1] physical pages of the split (paged caches)
     uint32_t heads;     // HeadState [G]
+    uint32_t own;       // fp32 [G][D] the finishing split's own partial output
     uint32_t total;
 };
 
 // Per wave, for one chunk of at most kTargetChunk targets of one head.
 struct TargetArea {
     double tau[kTargetChunk];      // targets scaled by Z
-    int key[kTargetChunk];         // split-local key of each target (merge path)
+    int mark[kTargetChunk];        // list entry whose first target this is, else -1
     int lkey[kTargetChunk];        // distinct sampled keys, ascending
     unsigned int lcnt[kTargetChunk];   // samples of each of them
 };
@@ -94,7 +96,8 @@ __host__ __device__ inline LdsLayout lds_layout(int G, int D, int split, int nt)
     L.prefix = (uint32_t)((scratch + 15) & ~(size_t)15);
     L.pages = L.prefix + (uint32_t)(G * split * 8);
     L.heads = (L.pages + (uint32_t)((split / 16 + 1) * 4) + 15) & ~15u;
-    L.total = L.heads + (uint32_t)(G * sizeof(HeadState));
+    L.own = L.heads + (uint32_t)(G * sizeof(HeadState));
+    L.total = L.own + (uint32_t)(G * D * 4);
     return L;
 }
 
@@ -239,49 +242,95 @@ __device__ __forceinline__ void stream_scores(const Params& p, const Item& it, f
     }
 }
 
+// Record of split t of query head hq of sequence b: one 64-bit word
+// (l_t bits << 32 | m_t bits), written and read as a single atomic word.  A
+// split with keys has l_t >= 1 (its maximum contributes exp(0)), so a record
+// is written exactly when its high half is nonzero; records are zero between
+// calls.
+__device__ __forceinline__ unsigned long long* record_of(const Params& p, int b, int hq, int t) {
+    return p.records + ((int64_t)b * p.Hq + hq) * p.T + t;
+}
+
 // ---------------------------------------------------------------------------
 // Split statistics and the in-split prefix (one wave per head).  Lane L owns
-// keys [L*ept, (L+1)*ept), ept = split/64 <= 16; the loops over them stay
-// rolled (short, data-dependent trip counts).
+// keys [L*EPT, (L+1)*EPT), EPT = split/64 in {1, 2, 4, 8, 16}, read and
+// written with vector LDS accesses.  With PUBLISH the head's wave stores its
+// record as soon as m_t and l_t are known (no workgroup barrier first: a
+// reader re-reads a record until it is written), then writes the prefix.
 // ---------------------------------------------------------------------------
-template <int G, int NT>
-__device__ __forceinline__ void split_stats(const Params& p, const Item& it, const float* sc,
-                                            uint64_t* prefix, HeadState* hs) {
+template <int G, int NT, int EPT, bool PUBLISH>
+__device__ __forceinline__ void split_stats_t(const Params& p, const Item& it, const float* sc,
+                                              uint64_t* prefix, HeadState* hs) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int split = p.split;
-    const int ept = split >> 6;
-    const int i0 = lane * ept;
-    const int n_own = max(0, min(ept, it.ns - i0));    // keys of this lane inside the split
+    const int split = EPT * 64;
+    const int i0 = lane * EPT;
+    const int n_own = max(0, min(EPT, it.ns - i0));    // keys of this lane inside the split
     for (int h = wave; h < G; h += NW) {
+        float s[EPT];
         const float* row = sc + h * split + i0;
-        uint64_t* ph = prefix + h * split + i0;
+        if constexpr (EPT >= 4) {
+#pragma unroll
+            for (int k = 0; k < EPT; k += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(row + k);
+                s[k] = v.x; s[k + 1] = v.y; s[k + 2] = v.z; s[k + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) s[k] = row[k];
+        }
         float mx = -INFINITY;
-#pragma unroll 4
-        for (int k = 0; k < n_own; ++k) mx = fmaxf(mx, row[k]);
+#pragma unroll
+        for (int k = 0; k < EPT; ++k)
+            if (k < n_own) mx = fmaxf(mx, s[k]);
         mx = wave_max_f32(mx);
         // fixed-point masses and their in-lane inclusive prefix
-        uint64_t run = 0;
+        uint64_t run[EPT];
+        uint64_t acc = 0;
         int lastpos = -1;
-#pragma unroll 4
-        for (int k = 0; k < n_own; ++k) {
-            const uint64_t e = fixed_mass(mass_exp(row[k] - mx));
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const uint64_t e = (k < n_own) ? fixed_mass(mass_exp(s[k] - mx)) : 0;
             if (e) lastpos = i0 + k;
-            run += e;
-            ph[k] = run;
+            acc += e;
+            run[k] = acc;
         }
-        const uint64_t incl = wave_scan_add_u64(run);
-        const uint64_t excl = incl - run;
-#pragma unroll 4
-        for (int k = 0; k < n_own; ++k) ph[k] += excl;
+        const uint64_t incl = wave_scan_add_u64(acc);
+        const uint64_t excl = incl - acc;
         const uint64_t total = lane_u64(incl, 63);
         lastpos = wave_max_i32(lastpos);
         if (lane == 0) {
+            const float l = (float)fixed_to_double(total);
             hs[h].m_t = mx;
-            hs[h].l_t = (float)fixed_to_double(total);
+            hs[h].l_t = l;
             hs[h].lastpos = lastpos;
+            if constexpr (PUBLISH) {
+                const unsigned long long r = (unsigned long long)__float_as_uint(l) << 32 | __float_as_uint(mx);
+                __hip_atomic_store(record_of(p, it.b, it.g * G + h, it.t), r, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
+        uint64_t* ph = prefix + h * split + i0;
+        if constexpr (EPT >= 2) {
+#pragma unroll
+            for (int k = 0; k < EPT; k += 2)
+                *reinterpret_cast<ulonglong2*>(ph + k) = make_ulonglong2(excl + run[k], excl + run[k + 1]);
+        } else {
+            ph[0] = excl + run[0];
+        }
+    }
+}
+
+template <int G, int NT, bool PUBLISH>
+__device__ __forceinline__ void split_stats(const Params& p, const Item& it, const float* sc,
+                                            uint64_t* prefix, HeadState* hs) {
+    switch (p.split) {
+        case 64: split_stats_t<G, NT, 1, PUBLISH>(p, it, sc, prefix, hs); break;
+        case 128: split_stats_t<G, NT, 2, PUBLISH>(p, it, sc, prefix, hs); break;
+        case 256: split_stats_t<G, NT, 4, PUBLISH>(p, it, sc, prefix, hs); break;
+        case 512: split_stats_t<G, NT, 8, PUBLISH>(p, it, sc, prefix, hs); break;
+        default: split_stats_t<G, NT, 16, PUBLISH>(p, it, sc, prefix, hs); break;
     }
 }
 
@@ -296,23 +345,19 @@ __device__ __forceinline__ void systematic_offsets(const Params& p, const Item& 
     }
 }
 
-// Record of split t of query head hq of sequence b: one 64-bit word
-// (l_t bits << 32 | m_t bits), written and read as a single atomic word.  A
-// split with keys has l_t >= 1 (its maximum contributes exp(0)), so a record
-// is written exactly when its high half is nonzero; records are zero between
-// calls.
-__device__ __forceinline__ unsigned long long* record_of(const Params& p, int b, int hq, int t) {
-    return p.records + ((int64_t)b * p.Hq + hq) * p.T + t;
-}
-
-template <int G>
-__device__ __forceinline__ void publish_stats(const Params& p, const Item& it, const HeadState* hs) {
-    const int h = threadIdx.x;
-    if (h < G) {
-        const unsigned long long r =
-            (unsigned long long)__float_as_uint(hs[h].l_t) << 32 | __float_as_uint(hs[h].m_t);
-        __hip_atomic_store(record_of(p, it.b, it.g * G + h, it.t), r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---------------------------------------------------------------------------
+// Waits (one lane) until the device-coherent word *w satisfies `ready`, one
+// load at a time (more loads in flight from every waiting workgroup slowed the
+// memory traffic of the workgroups still streaming more than they saved).
+// Returns false after kSpinLimit loads.
+// ---------------------------------------------------------------------------
+template <typename Ready>
+__device__ __forceinline__ bool poll_until(const unsigned int* w, Ready&& ready) {
+    for (int iter = 0; iter < kSpinLimit; ++iter) {
+        if (ready(__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) return true;
+        __builtin_amdgcn_s_sleep(1);
     }
+    return false;
 }
 
 // ---------------------------------------------------------------------------
@@ -337,14 +382,9 @@ __device__ __forceinline__ bool group_barrier(const Params& p, const Item& it, O
                 __hip_atomic_store(bar + 32 * (2 + c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             const unsigned int* flag = bar + 32 * (2 + blockIdx.x % kFlagCopies);
-            for (int iter = 0;
-                 __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u; ++iter) {
-                if (iter >= kSpinLimit) {
-                    ok = 0;
-                    __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
+            if (!poll_until(flag, [](unsigned int v) { return v != 0u; })) {
+                ok = 0;
+                __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         s_ok = ok;
@@ -465,33 +505,40 @@ __device__ __forceinline__ void target_range(const Params& p, int b, int hq, dou
 
 // ---------------------------------------------------------------------------
 // Inverse-CDF sampling of targets [m0, m0 + na) of one head (one wave): each
-// target tau goes to the key j with C_j <= tau < C_{j+1} (half-open intervals,
-// Appendix A.4); a target past the split's last edge (rounding) goes to its
-// last key of positive mass.  Writes idx and leaves the distinct keys with
-// their sample counts, ascending, in ta->lkey / ta->lcnt; returns how many.
-//   few targets (<= 8): one at a time -- a ballot over the lanes' last edges finds
-//     the lane that owns the key, one LDS read per lane finds the key;
-//   many: a merge path of targets against edges, lane-parallel, then a
-//     run-length compaction of the keys.
+// target tau goes to the first key j of the split whose upper edge
+// C_{j+1} = W_t + exp(m_t - M) * P_j exceeds it (half-open intervals,
+// Appendix A.4); a target past every edge (rounding) goes to the split's last
+// key of positive mass.  Writes idx and leaves the distinct keys with their
+// sample counts, ascending, in ta->lkey / ta->lcnt; returns how many.
+//   few targets (<= 8): one at a time -- a ballot over the lanes' last edges
+//     (lane l owns keys [l*ept, (l+1)*ept)) finds the lane that owns the key,
+//     one LDS read per lane finds the key;
+//   more: by keys, 64 at a time (lane l takes key j0 + l): each lane counts
+//     the targets below its key's upper edge (+inf for the last key of
+//     positive mass), and the key holds the targets between that count and
+//     its left neighbour's.  For stratified and systematic targets the count
+//     is within one of a closed-form estimate (target m lies in stratum m)
+//     and is settled by one or two reads of the chunk's targets; for
+//     multinomial it is a binary search.  Every key with targets marks its
+//     first one, and a max-scan over the marks gives each target its key, so
+//     idx is written by all lanes at once.
 // ---------------------------------------------------------------------------
 template <int MODE>
 __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, const HeadState& st, int hq,
                                             const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
     const int ns = it.ns;
-    const int ept = p.split >> 6;
-    int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S;
+    int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S + m0;
     const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0);
     const int lastpos = max(st.lastpos, 0);
-    // upper edge of key j's interval: C_{j+1} = W_t + exp(m_t - M) * P_j
     auto edge = [&](int j) { return st.w_lo + st.f * fixed_to_double(ph[j]); };
-    int nlist = 0;
     if (na <= 8) {
+        const int ept = p.split >> 6;
         double my_tau = 0.0;
         if (lane < na) my_tau = ts.tau(m0 + lane);
         const int i0 = lane * ept;
         const int n_own = max(0, min(ept, ns - i0));
         const double lane_hi = n_own > 0 ? edge(i0 + n_own - 1) : INFINITY;
-        int prev = -1;
+        int prev = -1, nlist = 0;
         for (int k = 0; k < na; ++k) {
             const double t = __shfl(my_tau, k, 64);
             // lanes whose every key's interval ends at or below t
@@ -504,7 +551,7 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
                 local = c * ept + __popcll(__ballot(le));
             }
             if (lane == 0) {
-                idx_row[m0 + k] = it.key0 + local;
+                idx_row[k] = it.key0 + local;
                 if (local == prev) {
                     ta->lcnt[nlist - 1] += 1u;
                 } else {
@@ -518,56 +565,68 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
         wave_lds_sync();
         return nlist;
     }
-    for (int k = lane; k < na; k += 64) ta->tau[k] = ts.tau(m0 + k);
-    wave_lds_sync();
-    // lane takes an equal share of the merged sequence; an edge equal to a
-    // target comes first, so the target goes to the key above it
-    const int total = na + ns;
-    const int per = (total + 63) >> 6;
-    const int d0 = min(lane * per, total);
-    const int d1 = min(d0 + per, total);
-    int lo = max(0, d0 - ns), up = min(d0, na);
-    while (lo < up) {
-        const int mid = (lo + up) >> 1;
-        if (ta->tau[mid] < edge(d0 - 1 - mid)) lo = mid + 1;
-        else up = mid;
-    }
-    int i = lo, j = d0 - lo;
-    for (int d = d0; d < d1; ++d) {
-        if (i < na && (j >= ns || ta->tau[i] < edge(j))) {
-            const int local = (j < ns) ? j : lastpos;
-            idx_row[m0 + i] = it.key0 + local;
-            ta->key[i] = local;
-            ++i;
-        } else {
-            ++j;
-        }
+    for (int k = lane; k < na; k += 64) {
+        ta->tau[k] = ts.tau(m0 + k);
+        ta->mark[k] = -1;
     }
     wave_lds_sync();
-    // run-length compaction of the (non-decreasing) keys: first the start of
-    // every run, then each run's length from the start of the next
-    for (int c0 = 0; c0 < na; c0 += 64) {
-        const int m = c0 + lane;
-        const bool start = m < na && (m == 0 || ta->key[m - 1] != ta->key[m]);
-        const unsigned long long starts = __ballot(start);
-        if (start) {
-            const int pos = nlist + __popcll(starts & ((1ull << lane) - 1ull));
-            ta->lkey[pos] = ta->key[m];
-            ta->lcnt[pos] = (unsigned)m;
+    const double* tau = ta->tau;
+    const int nkeys = min(ns, lastpos + 1);      // keys after lastpos take nothing
+    const double s_over_z = (double)p.S / st.z;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int carry = 0;          // count below the upper edge of the key before j0
+    int nlist = 0;
+    for (int j0 = 0; j0 < nkeys; j0 += 64) {
+        const int j = j0 + lane;
+        int c = na;
+        if (j < lastpos) {
+            const double u = edge(j);
+            if constexpr (MODE == 0) {
+                int lo = 0, hi = na;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (tau[mid] < u) lo = mid + 1;
+                    else hi = mid;
+                }
+                c = lo;
+            } else {
+                const double est = u * s_over_z - (MODE == 2 ? st.u0 : 0.0);
+                const double e = fmin(fmax(MODE == 2 ? ceil(est) : floor(est), (double)m0), (double)(m0 + na));
+                int i = (int)e - m0;
+                while (i > 0 && tau[i - 1] >= u) --i;
+                while (i < na && tau[i] < u) ++i;
+                c = i;
+            }
         }
-        nlist += __popcll(starts);
+        int first = __shfl_up(c, 1, 64);
+        if (lane == 0) first = carry;
+        carry = __shfl(c, 63, 64);
+        const bool has = j < nkeys && c > first;
+        const unsigned long long bal = __ballot(has);
+        if (has) {
+            const int pos = nlist + __popcll(bal & below);
+            ta->lkey[pos] = j;
+            ta->lcnt[pos] = (unsigned)(c - first);
+            ta->mark[first] = pos;
+        }
+        nlist += __popcll(bal);
     }
     wave_lds_sync();
-    for (int q0 = 0; q0 < nlist; q0 += 64) {
-        const int q = q0 + lane;
-        unsigned int len = 0;
-        if (q < nlist) {
-            const unsigned int next = (q + 1 < nlist) ? ta->lcnt[q + 1] : (unsigned)na;
-            len = next - ta->lcnt[q];
-        }
-        wave_lds_sync();
-        if (q < nlist) ta->lcnt[q] = len;
-        wave_lds_sync();
+    // target i belongs to the list entry with the largest mark at or below i
+    // (target 0 is always marked); lane l scans targets [4l, 4l + 4)
+    int v[4], run = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane * 4 + k;
+        run = max(run, i < na ? ta->mark[i] : -1);
+        v[k] = run;
+    }
+    int before = __shfl_up(wave_scan_max_i32(run), 1, 64);
+    if (lane == 0) before = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane * 4 + k;
+        if (i < na) idx_row[i] = it.key0 + ta->lkey[max(before, v[k])];
     }
     wave_lds_sync();
     return nlist;
@@ -575,60 +634,84 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
 
 // ---------------------------------------------------------------------------
 // Sampling and gather-and-add for one head (one wave, no workgroup barrier).
-// Each distinct sampled key of a chunk of targets is gathered once, a whole V
-// row per wave-wide load (lane l holds elements [l*EL, (l+1)*EL)), weighted
-// by its sample count; all of a chunk's loads are issued before any is used.
-// The waves of a workgroup gather the rows of the same split at the same
-// time, so a row that several heads of the group sampled is fetched from HBM
-// once and served to the others from L2.
+// Each distinct sampled key of a chunk of targets is gathered once, weighted
+// by its sample count.  A V row is read by LPR = d*e/16 lanes with 16-byte
+// loads, so one wave-wide load covers RPL = 64/LPR rows and UL loads per lane
+// keep UL*RPL rows in flight; the row groups' partial sums are then combined
+// across lanes.  The waves of a workgroup gather the rows of the same split
+// at the same time, so a row that several heads of the group sampled is
+// fetched from HBM once and served to the others from L2.
 // ---------------------------------------------------------------------------
 template <int G, int D, typename E>
 __device__ __forceinline__ void sample_head(const Params& p, const Item& it, const HeadState& st, int h,
                                             const LdsLayout& L, unsigned char* smem) {
-    constexpr int EL = D / 64;                  // elements of a V row per lane
-    constexpr int U = 8;                        // rows in flight per wave
+    constexpr int LPR = D * E::bytes / 16;      // lanes per V row
+    constexpr int RPL = 64 / LPR;               // rows per wave-wide load
+    constexpr int ELV = 16 / E::bytes;          // elements per lane per row
+    constexpr int UL = 8;                       // loads in flight per lane
+    constexpr int EL = D / 64;                  // output elements added per lane
+    static_assert(RPL * LPR == 64 && ELV == EL * RPL, "row shape");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int rsub = lane / LPR;
+    const int piece = lane % LPR;
     const int hq = it.g * G + h;
     const uint64_t* ph = reinterpret_cast<const uint64_t*>(smem + L.prefix) + h * p.split;
     const int* pages = reinterpret_cast<const int*>(smem + L.pages);
     TargetArea* ta = reinterpret_cast<TargetArea*>(smem + L.scratch) + wave;
     const char* vbase = reinterpret_cast<const char*>(p.v);
 
-    float acc[EL];
+    float acc[ELV];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < ELV; ++e) acc[e] = 0.0f;
     for (int m0 = st.m_lo; m0 < st.m_hi; m0 += kTargetChunk) {
         const int na = min(kTargetChunk, st.m_hi - m0);
         int nlist;
         if (p.mode == 2) nlist = sample_chunk<2>(p, it, st, hq, ph, ta, m0, na, lane);
         else if (p.mode == 1) nlist = sample_chunk<1>(p, it, st, hq, ph, ta, m0, na, lane);
         else nlist = sample_chunk<0>(p, it, st, hq, ph, ta, m0, na, lane);
-        for (int r0 = 0; r0 < nlist; r0 += U) {
-            float x[U][EL];
-            float wgt[U];
+        for (int r0 = 0; r0 < nlist; r0 += UL * RPL) {
+            uint4 x[UL];
+            float wgt[UL];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UL; ++u) {
+                // a load whose rows all lie past the list is not issued (the
+                // test is the same in every lane); a row past the list within
+                // an issued load re-reads the first row with weight 0
                 wgt[u] = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EL; ++e) x[u][e] = 0.0f;
-                if (r0 + u < nlist) {
-                    const int64_t off = row_offset(p, it, ta->lkey[r0 + u], pages) + lane * EL;
-                    E::template load_row_part<EL>(vbase + off * E::bytes, x[u]);
-                    wgt[u] = (float)ta->lcnt[r0 + u];
+                x[u] = make_uint4(0u, 0u, 0u, 0u);
+                if (r0 + u * RPL < nlist) {
+                    const int row = r0 + u * RPL + rsub;
+                    const bool ok = row < nlist;
+                    const int key = ta->lkey[ok ? row : 0];
+                    wgt[u] = ok ? (float)ta->lcnt[row] : 0.0f;
+                    const int64_t off = row_offset(p, it, key, pages) + piece * ELV;
+                    x[u] = load16(vbase + off * E::bytes);
                 }
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < EL; ++e) acc[e] = fmaf(wgt[u], x[u][e], acc[e]);
+            for (int u = 0; u < UL; ++u) E::axpy16(wgt[u], x[u], acc);
         }
         wave_lds_sync();       // the next chunk reuses the target area
     }
-    float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D +
-                  lane * EL;
+    // combine the RPL row groups: afterwards every lane holds its piece's sums
 #pragma unroll
-    for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slot + e, acc[e]);
+    for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < ELV; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
+    // lane adds EL of its piece's ELV elements, so the 64 lanes cover the row
+    // once: into the group's accumulation slot, or, in the split that finishes
+    // the group's output, into its own partial in LDS
+    const int col = piece * ELV + rsub * EL;
+    if (it.t == kFinisherSplit) {
+        float* own = reinterpret_cast<float*>(smem + L.own) + h * D + col;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) own[e] = acc[rsub * EL + e];
+    } else {
+        float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D + col;
+#pragma unroll
+        for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slot + e, acc[rsub * EL + e]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -745,7 +828,12 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
         }
         wave_lds_sync();
         const HeadState st = hs[h];
-        if (st.m_hi > st.m_lo) sample_head<G, D, E>(p, it, st, h, L, smem);
+        if (st.m_hi > st.m_lo) {
+            sample_head<G, D, E>(p, it, st, h, L, smem);
+        } else if (it.t == kFinisherSplit) {
+            float* own = reinterpret_cast<float*>(smem + L.own) + h * D;
+            for (int i = lane; i < D; i += 64) own[i] = 0.0f;
+        }
     }
     return ok_all;
 }
@@ -755,29 +843,38 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ---------------------------------------------------------------------------
 // The output of a (sequence, KV head) and the clean-up of its workspace state.
-// Each split, once its additions into the accumulation slots have completed,
-// counts itself done.  The last one -- every other split of the group has then
-// passed the barrier and read the records and targets -- sums the kOutSlots
-// slots, stores o = (1/S) * sum (Eq. 3) for the G heads, and returns to zero
-// the slots, the barrier flags, the group's split records and (multinomial) its
-// targets, so that a completed call leaves this state all zero.
+// Split kFinisherSplit finishes the group: it kept its own partial output in
+// LDS, waits until the other Tb - 1 splits have counted themselves done (each
+// once its additions into the accumulation slots have completed), sums the
+// kOutSlots slots and its own partial, stores o = (1/S) * sum (Eq. 3) for the
+// G heads, and returns the slots, the counts, the barrier flags, the group's
+// split records and (multinomial) its targets to zero.  Split 0 is the one
+// that holds a sequence's first keys, where attention sinks put much of the
+// mass and hence most samples, so it tends to be the group's last split to
+// finish sampling anyway.  Returns false if the wait gave up.
 // ---------------------------------------------------------------------------
 template <int G, int D, int NT>
-__device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
-    __shared__ int s_last;
-    wait_memory();           // this wave's slot additions have been performed
-    __syncthreads();
+__device__ __forceinline__ bool finish_output(const Params& p, const Item& it, const LdsLayout& L,
+                                              unsigned char* smem) {
+    __shared__ int s_ok;
     unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
-    if (threadIdx.x == 0) {
-        const unsigned int prev = __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = prev == (unsigned int)it.Tb - 1u;
+    if (it.t != kFinisherSplit) {
+        wait_memory();           // this wave's slot additions have been performed
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
     }
-    __syncthreads();
-    if (!s_last) return;
+    if (threadIdx.x == 0) {
+        const unsigned int others = (unsigned int)it.Tb - 1u;
+        s_ok = others == 0u || poll_until(bar + 32, [others](unsigned int v) { return v == others; });
+        if (!s_ok) __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();             // also orders the waves' own partials in LDS
     // slot words in pairs: the 16 loads of a pair are all in flight at once
     constexpr int NP = G * D / 2;
     unsigned long long* acc =
         reinterpret_cast<unsigned long long*>(p.accum + ((int64_t)it.b * p.Hkv + it.g) * kOutSlots * G * D);
+    const float2* own = reinterpret_cast<const float2*>(smem + L.own);
     float* o = p.o + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D;
     const float inv_s = 1.0f / (float)p.S;
     for (int i = threadIdx.x; i < NP; i += NT) {
@@ -785,7 +882,8 @@ __device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
 #pragma unroll
         for (int k = 0; k < kOutSlots; ++k)
             v[k] = __hip_atomic_load(acc + k * NP + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float s0 = 0.0f, s1 = 0.0f;
+        const float2 mine = own[i];
+        float s0 = mine.x, s1 = mine.y;
 #pragma unroll
         for (int k = 0; k < kOutSlots; ++k) {
             s0 += __uint_as_float((uint32_t)v[k]);
@@ -808,6 +906,7 @@ __device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
         double* tg = p.targets + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
         for (int i = threadIdx.x; i < G * p.S; i += NT) tg[i] = 0.0;
     }
+    return s_ok != 0;
 }
 
 // o = 0 and idx = -1 for the G heads of an empty sequence.

@@ -107,6 +107,7 @@ def test_default_split_keeps_splits_per_sequence_bounded(lib):
     (dict(), 8192, 0, OK),
     (dict(), 65535, 1, OK),
     (dict(split_size=100), 256, 2, INVALID),
+    (dict(split_size=192), 256, 2, INVALID),                # not a power of two
     (dict(split_size=2048), 256, 2, INVALID),
     (dict(page_size=8, pages_per_seq=4096, num_pages=4096), 256, 2, INVALID),
     (dict(page_size=24, pages_per_seq=4096, num_pages=4096), 256, 2, INVALID),
