@@ -35,7 +35,7 @@ __device__ __forceinline__ void fused_item(const Params& p, const Item& it, cons
     split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     group_barrier(p, it, [&] { systematic_offsets<G, 1>(p, it, hs); });
     prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit);
-    finish_output<G, D, NT>(p, it, L, smem);
+    finish_output<G, D, NT>(p, it);
 }
 
 // Four waves per SIMD (all 1024 splits of a batch-1, 8-KV-head, 32k-token

@@ -30,8 +30,8 @@ constexpr size_t kSyncBytes = sizeof(SyncWords);
 // between calls:
 //   line 0 word 0: splits that have published their records this call (the
 //                  last one resets it);
-//   line 1 word 0: splits other than the finishing one that have added their
-//                  output this call (the finishing split resets it);
+//   line 1 word 0: splits that have added their output this call (the last one
+//                  finishes the output and resets it);
 //   lines 2 .. 1+kFlagCopies: copies of a flag raised to 1 once all splits
 //                  published (a waiting workgroup polls copy
 //                  blockIdx % kFlagCopies, so no line is polled by many).
@@ -43,8 +43,6 @@ constexpr int kBarrierStride = 32 * kBarrierLines;   // 32-bit words per (sequen
 // (split % kOutSlots) of its (sequence, KV head), so few additions meet on one
 // word; the last split to finish sums the slots into o and clears them.
 constexpr int kOutSlots = 16;
-// The split of each (sequence, KV head) that finishes its output.
-constexpr int kFinisherSplit = 0;
 
 struct Params {
     const void* q;

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(NT) void sample_kernel(Params p) {
     // the records come from the score pass, an earlier launch: one missing now
     // means no score pass preceded this one, which is an error, not a wait
     prefix_and_sample<G, D, E, NT>(p, it, L, smem, 0);
-    finish_output<G, D, NT>(p, it, L, smem);
+    finish_output<G, D, NT>(p, it);
 }
 
 template <int G, int D, typename E>

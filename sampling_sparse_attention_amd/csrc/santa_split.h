@@ -36,10 +36,17 @@ struct Item {
     int Tb;        // splits of sequence b
 };
 
+// Work items are numbered (sequence, KV head)-fastest: item = t * B * Hkv +
+// b * Hkv + g.  Every group then streams its splits across the whole launch,
+// so the groups reach their barriers together at the end of the K stream and
+// their latency-bound tails run side by side, instead of the tails of early
+// groups slowing the K stream of later ones.  With B * Hkv a multiple of 8 the
+// splits of a group also share one XCD.
 __device__ __forceinline__ Item item_coords(const Params& p, int item) {
     Item it;
-    it.t = item % p.T;
-    const int grp = item / p.T;
+    const int ng = p.B * p.Hkv;
+    it.t = item / ng;
+    const int grp = item - it.t * ng;
     it.g = grp % p.Hkv;
     it.b = grp / p.Hkv;
     return it;
@@ -75,7 +82,6 @@ struct LdsLayout {
     uint32_t prefix;    // u64 [G][split] in-split inclusive prefix of fixed-point masses
     uint32_t pages;     // int [split/16 + 1] physical pages of the split (paged caches)
     uint32_t heads;     // HeadState [G]
-    uint32_t own;       // fp32 [G][D] the finishing split's own partial output
     uint32_t total;
 };
 
@@ -96,8 +102,7 @@ __host__ __device__ inline LdsLayout lds_layout(int G, int D, int split, int nt)
     L.prefix = (uint32_t)((scratch + 15) & ~(size_t)15);
     L.pages = L.prefix + (uint32_t)(G * split * 8);
     L.heads = (L.pages + (uint32_t)((split / 16 + 1) * 4) + 15) & ~15u;
-    L.own = L.heads + (uint32_t)(G * sizeof(HeadState));
-    L.total = L.own + (uint32_t)(G * D * 4);
+    L.total = L.heads + (uint32_t)(G * sizeof(HeadState));
     return L;
 }
 
@@ -699,19 +704,11 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
     for (int m = LPR; m < 64; m <<= 1)
 #pragma unroll
         for (int e = 0; e < ELV; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
-    // lane adds EL of its piece's ELV elements, so the 64 lanes cover the row
-    // once: into the group's accumulation slot, or, in the split that finishes
-    // the group's output, into its own partial in LDS
-    const int col = piece * ELV + rsub * EL;
-    if (it.t == kFinisherSplit) {
-        float* own = reinterpret_cast<float*>(smem + L.own) + h * D + col;
+    // lane adds EL of its piece's ELV elements, so the 64 lanes cover the row once
+    float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D +
+                  piece * ELV + rsub * EL;
 #pragma unroll
-        for (int e = 0; e < EL; ++e) own[e] = acc[rsub * EL + e];
-    } else {
-        float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D + col;
-#pragma unroll
-        for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slot + e, acc[rsub * EL + e]);
-    }
+    for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slot + e, acc[rsub * EL + e]);
 }
 
 // ---------------------------------------------------------------------------
@@ -828,12 +825,7 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
         }
         wave_lds_sync();
         const HeadState st = hs[h];
-        if (st.m_hi > st.m_lo) {
-            sample_head<G, D, E>(p, it, st, h, L, smem);
-        } else if (it.t == kFinisherSplit) {
-            float* own = reinterpret_cast<float*>(smem + L.own) + h * D;
-            for (int i = lane; i < D; i += 64) own[i] = 0.0f;
-        }
+        if (st.m_hi > st.m_lo) sample_head<G, D, E>(p, it, st, h, L, smem);
     }
     return ok_all;
 }
@@ -843,38 +835,30 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 // ---------------------------------------------------------------------------
 // The output of a (sequence, KV head) and the clean-up of its workspace state.
-// Split kFinisherSplit finishes the group: it kept its own partial output in
-// LDS, waits until the other Tb - 1 splits have counted themselves done (each
-// once its additions into the accumulation slots have completed), sums the
-// kOutSlots slots and its own partial, stores o = (1/S) * sum (Eq. 3) for the
-// G heads, and returns the slots, the counts, the barrier flags, the group's
-// split records and (multinomial) its targets to zero.  Split 0 is the one
-// that holds a sequence's first keys, where attention sinks put much of the
-// mass and hence most samples, so it tends to be the group's last split to
-// finish sampling anyway.  Returns false if the wait gave up.
+// Each split, once its additions into the accumulation slots have completed,
+// counts itself done.  The last one -- every other split of the group has then
+// passed the barrier and read the records and targets -- sums the kOutSlots
+// slots, stores o = (1/S) * sum (Eq. 3) for the G heads, and returns to zero
+// the slots, the counts, the barrier flags, the group's split records and
+// (multinomial) its targets, so that a completed call leaves this state all
+// zero.  Nothing here waits for another workgroup.
 // ---------------------------------------------------------------------------
 template <int G, int D, int NT>
-__device__ __forceinline__ bool finish_output(const Params& p, const Item& it, const LdsLayout& L,
-                                              unsigned char* smem) {
-    __shared__ int s_ok;
+__device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
+    __shared__ int s_last;
+    wait_memory();           // this wave's slot additions have been performed
+    __syncthreads();
     unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
-    if (it.t != kFinisherSplit) {
-        wait_memory();           // this wave's slot additions have been performed
-        __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return true;
-    }
     if (threadIdx.x == 0) {
-        const unsigned int others = (unsigned int)it.Tb - 1u;
-        s_ok = others == 0u || poll_until(bar + 32, [others](unsigned int v) { return v == others; });
-        if (!s_ok) __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned int prev = __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned int)it.Tb - 1u;
     }
-    __syncthreads();             // also orders the waves' own partials in LDS
+    __syncthreads();
+    if (!s_last) return;
     // slot words in pairs: the 16 loads of a pair are all in flight at once
     constexpr int NP = G * D / 2;
     unsigned long long* acc =
         reinterpret_cast<unsigned long long*>(p.accum + ((int64_t)it.b * p.Hkv + it.g) * kOutSlots * G * D);
-    const float2* own = reinterpret_cast<const float2*>(smem + L.own);
     float* o = p.o + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D;
     const float inv_s = 1.0f / (float)p.S;
     for (int i = threadIdx.x; i < NP; i += NT) {
@@ -882,8 +866,7 @@ __device__ __forceinline__ bool finish_output(const Params& p, const Item& it, c
 #pragma unroll
         for (int k = 0; k < kOutSlots; ++k)
             v[k] = __hip_atomic_load(acc + k * NP + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float2 mine = own[i];
-        float s0 = mine.x, s1 = mine.y;
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
         for (int k = 0; k < kOutSlots; ++k) {
             s0 += __uint_as_float((uint32_t)v[k]);
@@ -906,7 +889,6 @@ __device__ __forceinline__ bool finish_output(const Params& p, const Item& it, c
         double* tg = p.targets + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
         for (int i = threadIdx.x; i < G * p.S; i += NT) tg[i] = 0.0;
     }
-    return s_ok != 0;
 }
 
 // o = 0 and idx = -1 for the G heads of an empty sequence.
