@@ -72,6 +72,7 @@ struct Params {
     int32_t split;                // keys per split, multiple of 64
     int32_t T;                    // splits per sequence: ceil(n_max / split)
     int32_t items;                // B * Hkv * T work items (one workgroup each)
+    int32_t head_fastest;         // item order: 1 (sequence, KV head)-fastest, 0 split-fastest
     int32_t S;
     int32_t mode;
 };

@@ -36,17 +36,26 @@ struct Item {
     int Tb;        // splits of sequence b
 };
 
-// Work items are numbered (sequence, KV head)-fastest: item = t * B * Hkv +
-// b * Hkv + g.  Every group then streams its splits across the whole launch,
-// so the groups reach their barriers together at the end of the K stream and
-// their latency-bound tails run side by side, instead of the tails of early
-// groups slowing the K stream of later ones.  With B * Hkv a multiple of 8 the
-// splits of a group also share one XCD.
+// Work item numbering.  The fused kernel numbers items (sequence, KV
+// head)-fastest, item = t * B * Hkv + b * Hkv + g: every group then streams its
+// splits across the whole launch, the groups reach their barriers together at
+// the end of the K stream and their latency-bound tails run side by side,
+// instead of the tails of early groups slowing the K stream of later ones
+// (with B * Hkv a multiple of 8 the splits of a group also share one XCD).
+// The two-kernel path, whose grids are larger than the device, numbers them
+// split-fastest, item = (b * Hkv + g) * T + t, so that a group's splits run
+// close together in time.
 __device__ __forceinline__ Item item_coords(const Params& p, int item) {
     Item it;
-    const int ng = p.B * p.Hkv;
-    it.t = item / ng;
-    const int grp = item - it.t * ng;
+    int grp;
+    if (p.head_fastest) {
+        const int ng = p.B * p.Hkv;
+        it.t = item / ng;
+        grp = item - it.t * ng;
+    } else {
+        it.t = item % p.T;
+        grp = item / p.T;
+    }
     it.g = grp % p.Hkv;
     it.b = grp / p.Hkv;
     return it;
