@@ -176,10 +176,11 @@ santa_status santa_workspace_init(void* workspace, size_t workspace_bytes, void*
 
 /*
  * How santa_decode will run this problem on the current device: 1 = one fused
- * kernel (score pass, global budget and gather in one launch), 2 = the score
- * pass followed by the sample pass.  The fused kernel needs the device to hold
- * more of its workgroups at once than a sequence has splits.  Returns the
- * negated santa_status on error.  Queries the HIP runtime, touches no memory.
+ * kernel (score pass, global budget and gather in one launch), used when the
+ * device holds one workgroup per work item (sequence, KV head, split) at
+ * once; 2 = the score pass followed by the sample pass otherwise.  Returns
+ * the negated santa_status on error.  Queries the HIP runtime, touches no
+ * memory.
  */
 int32_t santa_decode_path(const santa_shape* shape, int32_t num_samples, int32_t mode);
 
@@ -216,13 +217,13 @@ santa_status santa_decode(const santa_shape* shape, const void* q, const void* k
  *
  * santa_score_pass: the score pass of section 3.2, Pass 1 -- fills the
  *   workspace's stash and records (and, for multinomial sampling, the sorted
- *   targets), and zeroes o.  Reads q, K, seq_lens, block_table.
+ *   targets).  Reads q, K, seq_lens, block_table.
  * santa_sample_pass: global partition function, budget allocation and
- *   parallel gather (section 3.2 steps 2-3) -- writes idx and accumulates o.
- *   Reads the workspace written by santa_score_pass, V, seq_lens, block_table.
- *   It must directly follow santa_score_pass with the same arguments on the
- *   same workspace (it waits, boundedly, for that call's records).
- * santa_decode runs either these two kernels or one fused kernel with the same
+ *   parallel gather (section 3.2 steps 2-3) -- writes idx and o.  Reads the
+ *   workspace written by santa_score_pass, V, seq_lens, block_table.  It must
+ *   directly follow santa_score_pass with the same arguments on the same
+ *   workspace; without that call's records it sets the error word.
+ * santa_decode runs either these two kernels or the fused kernel with the same
  * results (santa_decode_path says which).
  */
 santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,

@@ -169,6 +169,31 @@ def test_fused_and_two_kernel_paths_agree():
             assert santa.workspace_error(ws1) == 0 and santa.workspace_error(ws2) == 0
 
 
+def test_large_grid_repeated_calls_match_split_stages_and_oracle():
+    """A step with more work items than the device holds at once (two-kernel path):
+    the same indices as calling the score and sample passes directly, parity with the
+    oracle, and a workspace left all zero after several calls in a row."""
+    lens = (8192, 8000, 5000, 1, 0, 8191, 4096, 7777)
+    x = _inputs(lens=lens, seed=9)
+    S, split = 128, 64
+    shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len, split_size=split)
+    B, Hq, d = x["q"].shape
+    for mode in (0, 1, 2):
+        assert santa.santa_decode_path(shape, S, mode) == santa.PATH_TWO_KERNELS
+        ws = santa.allocate_workspace(shape, S, mode, "cuda")
+        for seed in (5, 6, 7):
+            o1 = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+            i1 = torch.empty((B, Hq, S), dtype=torch.int32, device="cuda")
+            santa.santa_decode(shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, seed, o1, i1, ws)
+            torch.cuda.synchronize()
+            assert santa.workspace_error(ws) == 0
+            assert torch.count_nonzero(ws) == 0
+            o2, i2, _, _ = H.run_hip(x, S, mode, seed=seed, split=split, stages="split")
+            assert torch.equal(i1.cpu(), i2)
+            assert torch.allclose(o1.cpu(), o2, rtol=1e-5, atol=1e-6)
+        H.check_all(x, S, mode, 7, o1.cpu(), i1.cpu())
+
+
 def test_workspace_reused_across_calls_and_shapes():
     """Calls leave the workspace zero, so one workspace serves many calls of different shapes in a row,
     mixing the fused kernel and the two halves."""
