@@ -36,6 +36,24 @@ their reasons in the design notes of this repository):
 5. every query head of a GQA group samples independently (its own ``h`` in the
    counter);
 6. a sequence of length 0 gives ``o = 0`` and ``idx = -1``.
+
+It also computes S^2ANTA-flash (§3.3 of the same page: a fixed, uniform budget
+per tile, local sampling as if the tile held all the mass, and a final merge
+that down-weights each tile's partial output by its share of the true
+partition function).  The pseudocode appendix it points to is not in the
+pages; the readings taken are
+
+7. a tile is ``tile`` consecutive keys of the sequence (the score pass's
+   split), so a sequence of ``n`` keys has ``T = ceil(n / tile)`` tiles;
+8. the tiles share exactly ``S`` samples, tile ``t`` taking ``floor(S / T)``
+   plus one for ``t < S mod T`` (uniform up to one, and ``idx`` keeps ``S``
+   entries, tile by tile); ``S >= T``, so every tile is sampled and the
+   estimator stays unbiased;
+9. tile ``t`` applies the chosen rule with its own ``S_t`` to its own softmax
+   (the same targets and inverse CDF as above), drawing its uniforms from the
+   Philox counter ``(j, h, b, 1 + t)``;
+10. ``o = sum_t (Z_t / Z) * (1/S_t) * sum_j V[idx_tj]``, where ``Z_t`` is the
+    tile's partition function and ``Z`` their sum.
 """
 from __future__ import annotations
 
@@ -200,6 +218,103 @@ def sequence_keys(cache: np.ndarray, n: int, b: int, block_table, page_size: int
     i = np.arange(n)
     pages = np.asarray(block_table)[b, i // page_size]
     return np.asarray(cache)[pages, i % page_size]
+
+
+# ---------------------------------------------------------------------------
+# S^2ANTA-flash (§3.3; readings 7-10 above), one query head at a time.
+# ---------------------------------------------------------------------------
+def tile_uniforms(seed: int, b: int, h: int, t: int, j) -> np.ndarray:
+    """U[0, 1) draws ``j`` (array) of tile ``t`` of query head ``h`` of sequence ``b``
+    (reading 9: counter ``(j, h, b, 1 + t)``, a stream of its own per tile)."""
+    j = np.asarray(j, dtype=np.uint64)
+    w0, _, _, _ = philox4x64((j, np.uint64(h), np.uint64(b), np.uint64(1 + t)), (seed, 0))
+    return (w0 >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+
+
+def tile_budgets(S: int, T: int) -> np.ndarray:
+    """Samples of each of ``T`` tiles: ``S`` in all, uniform up to one (reading 8)."""
+    if S < T:
+        raise ValueError(f"S = {S} < {T} tiles: a tile without samples would bias the estimate")
+    return np.array([S // T + (1 if t < S % T else 0) for t in range(T)], dtype=np.int64)
+
+
+def sample_head_flash(s: np.ndarray, S: int, mode: int, seed: int, b: int, h: int, tile: int):
+    """S^2ANTA-flash's sampling for one query head from its scores ``s``.
+
+    Returns a dict: ``idx`` (``[S]``, tile by tile, each tile's keys in ascending
+    target order), ``tile_of`` (the tile of each sample), ``budget`` (``S_t``),
+    ``weight`` (``Z_t / Z``), ``t`` (each sample's target in its tile's unit
+    interval), ``F`` (the list of the tiles' local CDFs) and ``delta`` (boundary
+    distances in the local CDFs).
+    """
+    s = np.asarray(s, dtype=np.float64)
+    n = len(s)
+    T = -(-n // tile)
+    budget = tile_budgets(S, T)
+    M = s.max()
+    Zt = np.array([math.fsum(np.exp(s[t * tile:(t + 1) * tile] - M)) for t in range(T)])
+    idx, tile_of, targets, delta, Fs = [], [], [], [], []
+    for t in range(T):
+        st = s[t * tile:(t + 1) * tile]
+        p = softmax(st)                       # the tile as if it held all the mass
+        F = cdf(p)
+        u = tile_uniforms(seed, b, h, t, np.arange(draws_needed(mode, int(budget[t]))))
+        tt = targets_from_uniforms(mode, u, int(budget[t]))
+        local = inverse_cdf(F, p, tt)
+        idx.append(t * tile + local)
+        tile_of.append(np.full(len(local), t, dtype=np.int64))
+        targets.append(tt)
+        delta.append(boundary_distance(F, local, tt))
+        Fs.append(F)
+    return dict(idx=np.concatenate(idx), tile_of=np.concatenate(tile_of), budget=budget,
+                weight=Zt / math.fsum(Zt), t=np.concatenate(targets), delta=np.concatenate(delta), F=Fs)
+
+
+def estimate_flash(values: np.ndarray, idx: np.ndarray, tile_of: np.ndarray, budget: np.ndarray,
+                   weight: np.ndarray) -> np.ndarray:
+    """The deferred-normalisation merge (reading 10): each tile's mean of its sampled
+    rows, weighted by the tile's share ``Z_t / Z`` of the partition function."""
+    values = np.asarray(values, dtype=np.float64)
+    o = np.zeros(values.shape[1])
+    for t in range(len(budget)):
+        rows = values[np.asarray(idx)[tile_of == t]]
+        o += weight[t] * rows.sum(axis=0) / budget[t]
+    return o
+
+
+def decode_flash(q, k_cache, v_cache, seq_lens, block_table, page_size, S, mode, seed, tile,
+                 heads=None):
+    """S^2ANTA-flash decode for a batch of single-token queries; arguments as in
+    :func:`decode` plus the tile size.  Returns per-(b, h) dicts with ``o``,
+    ``idx`` (``[S]``), ``t``, ``delta``, ``tile_of`` and ``n``."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    G = Hq // Hkv
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hq)]
+    out = {}
+    rows_cache = {}
+    for b, h in heads:
+        n = int(seq_lens[b])
+        g = h // G
+        if n == 0:
+            out[(b, h)] = dict(o=np.zeros(d), idx=np.full(S, -1, dtype=np.int64), t=None,
+                               delta=None, tile_of=None, n=0)
+            continue
+        if (b, g) not in rows_cache:
+            rows_cache.clear()
+            keys = sequence_keys(k_cache, n, b, block_table, page_size)[:, g, :]
+            vals = sequence_keys(v_cache, n, b, block_table, page_size)[:, g, :]
+            rows_cache[(b, g)] = (np.asarray(keys, np.float64), np.asarray(vals, np.float64))
+        keys, vals = rows_cache[(b, g)]
+        s = scores(q[b, h], keys)
+        r = sample_head_flash(s, S, mode, seed, b, h, tile)
+        r["o"] = estimate_flash(vals, r["idx"], r["tile_of"], r["budget"], r["weight"])
+        r["n"] = n
+        r["s"] = s
+        out[(b, h)] = r
+    return out
 
 
 def decode(q, k_cache, v_cache, seq_lens, block_table, page_size, S, mode, seed,
