@@ -123,6 +123,9 @@ typedef struct santa_shape {
  *   accum    fp32 [B, Hkv, 16, G, d]: partial outputs, added by the splits of a
  *            (sequence, KV head) into slot (split % 16) and summed into o by
  *            the last of them;
+ *   flash    santa_decode_flash only: per (sequence, query head) a 64-bit
+ *            reference maximum, then (256-byte aligned) fp64 accumulators
+ *            [B, Hkv, 16, G, d + 2] of weighted tile means and weights;
  *   records  [B, Hq, num_splits] x 8 bytes: per split the maximum score m and
  *            l = sum exp(s_i - m) (the tile partition functions of section 3.2,
  *            Pass 1) as one word, fp32 l in the high and fp32 m in the low half
@@ -140,6 +143,7 @@ typedef struct santa_workspace_layout {
     size_t sync_offset;
     size_t barrier_offset;
     size_t accum_offset;
+    size_t flash_offset;
     size_t records_offset;
     size_t stash_offset;
     size_t stash_row_bytes;
@@ -226,6 +230,28 @@ santa_status santa_decode(const santa_shape* shape, const void* q, const void* k
  * santa_decode runs either these two kernels or the fused kernel with the same
  * results (santa_decode_path says which).
  */
+/*
+ * S^2ANTA-flash (section 3.3 of "Stochastic Sparse Attention for Memory-Bound
+ * Inference"): the same arguments and outputs as santa_decode, computed
+ * without the global budget.  The splits of santa_workspace_layout_query are
+ * the tiles: the T_b tiles of sequence b share the num_samples samples, tile
+ * t taking floor(num_samples / T_b) plus one for t < num_samples mod T_b
+ * (idx holds them tile by tile, each tile's in ascending target order); each
+ * tile samples by the given rule from its own softmax (Philox stream 1 + t,
+ * draw j at counter (j, h, b, 1 + t)), and
+ *     o = sum_t (Z_t / Z) * (1/S_t) * sum_j V[idx_tj],
+ * with Z_t the tile's partition function.  mode must be
+ * SANTA_MODE_STRATIFIED or SANTA_MODE_SYSTEMATIC and num_samples at least the
+ * number of splits (else SANTA_STATUS_UNSUPPORTED).  No workgroup waits for
+ * another, so every problem size runs as one kernel.  The weights are summed
+ * in fp64 relative to one split's maximum score, which needs the maximum
+ * scores of a sequence's tiles to lie within about 700 of each other.
+ */
+santa_status santa_decode_flash(const santa_shape* shape, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                                int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* seq_lens,
                               const int32_t* block_table, int32_t num_samples, int32_t mode,

@@ -18,7 +18,8 @@ __all__ = [
     "MODE_MULTINOMIAL", "MODE_STRATIFIED", "MODE_SYSTEMATIC", "Shape", "WorkspaceLayout",
     "SantaError", "library", "library_path", "make_shape", "santa_workspace_layout_query",
     "santa_workspace_size", "santa_workspace_init", "santa_decode_path", "santa_decode",
-    "santa_score_pass", "santa_sample_pass", "decode", "allocate_workspace", "workspace_error",
+    "santa_score_pass", "santa_sample_pass", "santa_decode_flash", "decode", "allocate_workspace",
+    "workspace_error",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -31,7 +32,7 @@ DTYPE_F32 = 1
 EXPORTED_SYMBOLS = (
     "santa_abi_version", "santa_status_string", "santa_last_error",
     "santa_workspace_layout_query", "santa_workspace_size", "santa_workspace_init",
-    "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass",
+    "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash",
 )
 PATH_FUSED = 1
 PATH_TWO_KERNELS = 2
@@ -58,6 +59,7 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [
         ("total_bytes", ctypes.c_size_t), ("sync_offset", ctypes.c_size_t),
         ("barrier_offset", ctypes.c_size_t), ("accum_offset", ctypes.c_size_t),
+        ("flash_offset", ctypes.c_size_t),
         ("records_offset", ctypes.c_size_t), ("stash_offset", ctypes.c_size_t),
         ("stash_row_bytes", ctypes.c_size_t), ("targets_offset", ctypes.c_size_t),
         ("split_size", ctypes.c_int32), ("num_splits", ctypes.c_int32),
@@ -95,7 +97,7 @@ def library() -> ctypes.CDLL:
         lib.santa_workspace_init.argtypes = [vp, sz, vp]
         lib.santa_decode_path.restype = i32
         lib.santa_decode_path.argtypes = [ctypes.POINTER(Shape), i32, i32]
-        for name in ("santa_decode", "santa_score_pass", "santa_sample_pass"):
+        for name in ("santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, sz, vp]
@@ -196,6 +198,13 @@ def santa_decode(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples,
                  workspace, stream=None) -> None:
     """One SANTA decode step (``santa_decode`` of the C ABI)."""
     _call("santa_decode", shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode,
+          seed, o, idx, workspace, stream)
+
+
+def santa_decode_flash(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o, idx,
+                       workspace, stream=None) -> None:
+    """One S^2ANTA-flash decode step (``santa_decode_flash`` of the C ABI)."""
+    _call("santa_decode_flash", shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode,
           seed, o, idx, workspace, stream)
 
 

@@ -122,8 +122,13 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     L.sync_offset = 0;
     L.barrier_offset = align256(santa::kSyncBytes);
     L.accum_offset = align256(L.barrier_offset + (size_t)s->batch * s->num_kv_heads * santa::kBarrierStride * 4);
-    L.records_offset = align256(L.accum_offset + (size_t)s->batch * s->num_q_heads * santa::kOutSlots *
-                                                     s->head_dim * sizeof(float));
+    L.flash_offset = align256(L.accum_offset + (size_t)s->batch * s->num_q_heads * santa::kOutSlots *
+                                                   s->head_dim * sizeof(float));
+    // flash region: reference maxima [B, Hq] u64, then (256-aligned) the fp64
+    // accumulators [B, Hkv, kOutSlots, G, d + 2]
+    L.records_offset = align256(L.flash_offset + align256(rows * sizeof(unsigned long long)) +
+                                (size_t)s->batch * s->num_q_heads * santa::kOutSlots * (s->head_dim + 2) *
+                                    sizeof(double));
     L.stash_offset = align256(L.records_offset + rows * (size_t)T * 8);
     L.stash_row_bytes = (size_t)T * split * sizeof(float);
     L.targets_offset = align256(L.stash_offset + rows * L.stash_row_bytes);
@@ -167,6 +172,8 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->records = reinterpret_cast<unsigned long long*>(w + L.records_offset);
     p->barrier = reinterpret_cast<unsigned int*>(w + L.barrier_offset);
     p->accum = reinterpret_cast<float*>(w + L.accum_offset);
+    p->flash_ref = reinterpret_cast<unsigned long long*>(w + L.flash_offset);
+    p->flash_acc = reinterpret_cast<double*>(w + L.flash_offset + align256((size_t)s->batch * s->num_q_heads * 8));
     p->stash = reinterpret_cast<float*>(w + L.stash_offset);
     p->targets = reinterpret_cast<double*>(w + L.targets_offset);
     p->stride_seq = s->kv_stride_seq;
@@ -332,6 +339,29 @@ santa_status santa_decode(const santa_shape* shape, const void* q, const void* k
                           void* workspace, size_t workspace_bytes, void* stream) {
     return run(kDecode, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o,
                idx, workspace, workspace_bytes, stream);
+}
+
+santa_status santa_decode_flash(const santa_shape* shape, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                                int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    santa::Params p;
+    Plan plan;
+    santa_status st = make_params(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o,
+                                  idx, workspace, workspace_bytes, &p, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    if (mode == SANTA_MODE_MULTINOMIAL)
+        return fail(SANTA_STATUS_UNSUPPORTED, "santa_decode_flash samples stratified or systematic (mode 1 or 2)");
+    if (num_samples < plan.T)
+        return fail(SANTA_STATUS_UNSUPPORTED,
+                    "santa_decode_flash needs a sample for every tile: num_samples %d < %d splits",
+                    num_samples, plan.T);
+    p.head_fastest = 1;
+    st = hip_check(santa::launch_flash(p, shape->dtype, static_cast<hipStream_t>(stream)),
+                   "launching the flash decode kernel");
+    if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
 }
 
 santa_status santa_score_pass(const santa_shape* shape, const void* q, const void* k_cache,

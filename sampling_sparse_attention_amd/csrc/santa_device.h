@@ -40,8 +40,10 @@ __device__ __forceinline__ uint64_t philox4x64_10_word0(uint64_t c0, uint64_t c1
 
 // U[0,1) on the 2^-53 grid for draw j of query head h of sequence b:
 // counter (j, h, b, 0), key (seed, 0).
-__device__ __forceinline__ double uniform01(uint64_t seed, int b, int h, uint64_t j) {
-    const uint64_t w = philox4x64_10_word0(j, (uint64_t)h, (uint64_t)b, 0ull, seed, 0ull);
+// Draw j of query head h of sequence b in stream `stream` (counter word 3:
+// 0 for SANTA's draws, 1 + t for tile t of S^2ANTA-flash).
+__device__ __forceinline__ double uniform01(uint64_t seed, int b, int h, uint64_t j, uint64_t stream = 0) {
+    const uint64_t w = philox4x64_10_word0(j, (uint64_t)h, (uint64_t)b, stream, seed, 0ull);
     return (double)(w >> 11) * 0x1p-53;
 }
 

@@ -56,6 +56,8 @@ struct Params {
     unsigned long long* records;  // [B, Hq, T] words: l bits << 32 | m bits (0: not written yet)
     unsigned int* barrier;        // [B * Hkv] x kBarrierStride words: counts, flags
     float* accum;                 // [B * Hkv][kOutSlots][G * D] partial outputs (zero between calls)
+    double* flash_acc;            // S^2ANTA-flash: [B * Hkv][kOutSlots][G][D + 2] weighted sums, weight
+    unsigned long long* flash_ref;   // S^2ANTA-flash: [B, Hq] reference maximum (1 << 32 | bits), 0 unset
     float* stash;                 // [B, Hq, T * split] scaled scores (two-kernel path)
     double* targets;              // [B, Hq, S] sorted uniforms (multinomial only)
     int64_t stride_seq;           // elements
@@ -90,6 +92,7 @@ hipError_t launch_score(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_sample(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_fused(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream);
+hipError_t launch_flash(const Params& p, int dtype, hipStream_t stream);
 // Workgroups of the fused kernel one compute unit can hold at once (0 on error).
 int fused_blocks_per_cu(const Params& p, int dtype);
 // Bytes of LDS one workgroup may use on gfx950.

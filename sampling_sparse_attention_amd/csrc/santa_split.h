@@ -81,7 +81,9 @@ struct HeadState {
     int m_lo;       // targets [m_lo, m_hi) fall into this split
     int m_hi;
     int lastpos;    // last key of positive mass in the split
-    int pad[3];
+    int n_targets;  // S of the target sequence (S, or the tile's budget in flash)
+    int stream;     // Philox stream of its draws (0, or 1 + t in flash)
+    int off;        // idx position of the sequence's first target (0, or the tile's in flash)
 };
 
 // Byte offsets of the dynamic LDS of a split workgroup.
@@ -417,22 +419,25 @@ __device__ __forceinline__ bool group_barrier(const Params& p, const Item& it, O
 // ---------------------------------------------------------------------------
 // MODE is a template argument so that no path evaluates another mode's
 // targets (the compiler would otherwise compute the stratified Philox draw
-// speculatively for every target).
+// speculatively for every target).  In S^2ANTA-flash a tile's S_t targets
+// are numbered off .. off + S_t - 1 in idx and drawn from the tile's stream;
+// for SANTA off = 0, S_t = S and the stream is 0.
 template <int MODE>
 struct TargetSeq {
     const double* sorted;
     double u0;
     double z;
     uint64_t seed;
-    int S, b, hq;
+    int S, off, stream, b, hq;
     __device__ __forceinline__ double tau(int m) const {
+        const int j = m - off;
         double t;
         if constexpr (MODE == 0) {
             t = sorted[m];
         } else if constexpr (MODE == 1) {
-            t = ((double)m + uniform01(seed, b, hq, (uint64_t)m)) / (double)S;
+            t = ((double)j + uniform01(seed, b, hq, (uint64_t)j, (uint64_t)stream)) / (double)S;
         } else {
-            t = ((double)m + u0) / (double)S;
+            t = ((double)j + u0) / (double)S;
         }
         return t * z;
     }
@@ -468,11 +473,14 @@ __device__ __forceinline__ int count_below(const TargetSeq<MODE>& ts, double x, 
 }
 
 template <int MODE>
-__device__ __forceinline__ TargetSeq<MODE> target_seq(const Params& p, int b, int hq, double z, double u0) {
+__device__ __forceinline__ TargetSeq<MODE> target_seq(const Params& p, int b, int hq, double z, double u0,
+                                                      int n_targets = -1, int off = 0, int stream = 0) {
     TargetSeq<MODE> ts;
     ts.sorted = p.targets + ((int64_t)b * p.Hq + hq) * p.S;
     ts.seed = p.seed;
-    ts.S = p.S;
+    ts.S = n_targets < 0 ? p.S : n_targets;
+    ts.off = off;
+    ts.stream = stream;
     ts.b = b;
     ts.hq = hq;
     ts.u0 = u0;
@@ -542,7 +550,7 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
                                             const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
     const int ns = it.ns;
     int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S + m0;
-    const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0);
+    const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0, st.n_targets, st.off, st.stream);
     const int lastpos = max(st.lastpos, 0);
     auto edge = [&](int j) { return st.w_lo + st.f * fixed_to_double(ph[j]); };
     if (na <= 8) {
@@ -586,7 +594,7 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
     wave_lds_sync();
     const double* tau = ta->tau;
     const int nkeys = min(ns, lastpos + 1);      // keys after lastpos take nothing
-    const double s_over_z = (double)p.S / st.z;
+    const double s_over_z = (double)ts.S / st.z;
     const unsigned long long below = (1ull << lane) - 1ull;
     int carry = 0;          // count below the upper edge of the key before j0
     int nlist = 0;
@@ -604,7 +612,7 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
                 }
                 c = lo;
             } else {
-                const double est = u * s_over_z - (MODE == 2 ? st.u0 : 0.0);
+                const double est = ts.off + (u * s_over_z - (MODE == 2 ? st.u0 : 0.0));
                 const double e = fmin(fmax(MODE == 2 ? ceil(est) : floor(est), (double)m0), (double)(m0 + na));
                 int i = (int)e - m0;
                 while (i > 0 && tau[i - 1] >= u) --i;
@@ -656,9 +664,12 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
 // at the same time, so a row that several heads of the group sampled is
 // fetched from HBM once and served to the others from L2.
 // ---------------------------------------------------------------------------
-template <int G, int D, typename E>
+// The head's sum of count-weighted rows goes to emit(col, vals): every lane
+// passes D/64 consecutive elements starting at column col, and the 64 lanes
+// cover the row once.
+template <int G, int D, typename E, typename Emit>
 __device__ __forceinline__ void sample_head(const Params& p, const Item& it, const HeadState& st, int h,
-                                            const LdsLayout& L, unsigned char* smem) {
+                                            const LdsLayout& L, unsigned char* smem, Emit&& emit) {
     constexpr int LPR = D * E::bytes / 16;      // lanes per V row
     constexpr int RPL = 64 / LPR;               // rows per wave-wide load
     constexpr int ELV = 16 / E::bytes;          // elements per lane per row
@@ -713,11 +724,11 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
     for (int m = LPR; m < 64; m <<= 1)
 #pragma unroll
         for (int e = 0; e < ELV; ++e) acc[e] += __shfl_xor(acc[e], m, 64);
-    // lane adds EL of its piece's ELV elements, so the 64 lanes cover the row once
-    float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D +
-                  piece * ELV + rsub * EL;
+    // lane passes EL of its piece's ELV elements, so the 64 lanes cover the row once
+    float vals[EL];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slot + e, acc[rsub * EL + e]);
+    for (int e = 0; e < EL; ++e) vals[e] = acc[rsub * EL + e];
+    emit(piece * ELV + rsub * EL, vals);
 }
 
 // ---------------------------------------------------------------------------
@@ -831,10 +842,20 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
             hs[h].f = (double)mass_exp(hs[h].m_t - M);
             hs[h].m_lo = m_lo;
             hs[h].m_hi = max(m_hi, m_lo);
+            hs[h].n_targets = p.S;
+            hs[h].stream = 0;
+            hs[h].off = 0;
         }
         wave_lds_sync();
         const HeadState st = hs[h];
-        if (st.m_hi > st.m_lo) sample_head<G, D, E>(p, it, st, h, L, smem);
+        if (st.m_hi > st.m_lo) {
+            // into accumulation slot t mod 16 of the group
+            float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D;
+            sample_head<G, D, E>(p, it, st, h, L, smem, [&](int col, const float* vals) {
+#pragma unroll
+                for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, vals[e]);
+            });
+        }
     }
     return ok_all;
 }

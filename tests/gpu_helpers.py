@@ -126,4 +126,67 @@ def check_all(x: dict, S: int, mode: int, seed: int, o: torch.Tensor, idx: torch
     return rep
 
 
+def run_flash(x: dict, S: int, mode: int, seed: int, split: int = 0, workspace=None):
+    """Runs santa_decode_flash on the tensors of ``x``; returns o, idx, workspace, tile size."""
+    shape = santa.make_shape(x["q"], x["k"], x["block_table"], max_seq_len=x["workload"].seq_len,
+                             split_size=split)
+    B, Hq, d = x["q"].shape
+    o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=x["q"].device)
+    idx = torch.full((B, Hq, S), -7, dtype=torch.int32, device=x["q"].device)
+    ws = workspace if workspace is not None else santa.allocate_workspace(shape, S, mode, x["q"].device)
+    santa.santa_decode_flash(shape, x["q"], x["k"], x["v"], x["seq_lens"], x["block_table"], S, mode, seed,
+                             o, idx, ws)
+    torch.cuda.synchronize()
+    tile = santa.santa_workspace_layout_query(shape, S, mode).split_size
+    return o.cpu(), idx.cpu(), ws, tile
+
+
+def check_flash(x: dict, S: int, mode: int, seed: int, tile: int, o: torch.Tensor, idx: torch.Tensor,
+                heads=None) -> ParityReport:
+    """S^2ANTA-flash parity: idx exact outside the boundary window of each tile's local CDF;
+    o within O_REL_L2 of the oracle's fp64 merge of the GPU's own idx."""
+    w = x["workload"]
+    rep = ParityReport()
+    lens = x["seq_lens"].cpu()
+    if heads is None:
+        heads = [(b, h) for b in range(w.batch) for h in range(w.q_heads)]
+    rows_cache = {}
+    for b, h in heads:
+        n = int(lens[b])
+        where = f"flash (b={b}, h={h}, mode={mode}, S={S}, tile={tile})"
+        if n == 0:
+            assert torch.all(idx[b, h] == -1) and torch.all(o[b, h] == 0), f"empty sequence {b}"
+            continue
+        g = h // w.group
+        if (b, g) not in rows_cache:
+            rows_cache.clear()
+            rows_cache[(b, g)] = head_rows(x, b, g)
+        k, v = rows_cache[(b, g)]
+        s = O.scores(x["q"][b, h].double().cpu().numpy(), k)
+        ref = O.sample_head_flash(s, S, mode, seed, b, h, tile)
+        ig = idx[b, h].numpy().astype(np.int64)
+        rep.heads += 1
+        rep.targets += S
+        assert ig.min() >= 0 and ig.max() < n, f"{where}: index out of range"
+        assert np.all(ig // tile == ref["tile_of"]), f"{where}: a sample left its tile"
+        near = ref["delta"] < BOUNDARY_WINDOW
+        rep.boundary += int(near.sum())
+        bad = ig != ref["idx"]
+        far_bad = bad & ~near
+        assert not far_bad.any(), (f"{where}: {int(far_bad.sum())} indices differ away from a boundary, "
+                                   f"first at m={int(np.nonzero(far_bad)[0][0])}")
+        for m in np.nonzero(bad)[0]:
+            t = int(ref["tile_of"][m])
+            F = ref["F"][t]
+            lk = int(ig[m]) - t * tile
+            assert F[lk] - BOUNDARY_WINDOW <= ref["t"][m] < F[lk + 1] + BOUNDARY_WINDOW, \
+                f"{where}: a boundary-case index is not adjacent to its target"
+            rep.boundary_mismatch += 1
+        own = O.estimate_flash(v, ig, ref["tile_of"], ref["budget"], ref["weight"])
+        err = float(np.linalg.norm(o[b, h].double().numpy() - own) / max(np.linalg.norm(own), 1e-30))
+        rep.worst_rel_l2 = max(rep.worst_rel_l2, err)
+        assert err <= O_REL_L2, f"{where}: o relative L2 error {err:.3e}"
+    return rep
+
+
 unique_v_rows = W.unique_v_rows

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert len(declared) == 10
+    assert len(declared) == 11
     out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (santa_\w+)", out))
@@ -175,3 +175,24 @@ def test_decode_rejects_bad_pointers_before_launch(lib):
         assert f(ctypes.byref(shape), None, fake, fake, fake, None, 64, 2, ctypes.c_uint64(0),
                  fake, fake, fake, need, None) == INVALID
     del args
+
+
+def test_flash_rejects_multinomial_and_too_few_samples_before_launch(lib):
+    """santa_decode_flash samples by tiles: stratified or systematic only, and at
+    least one sample per tile; both are checked on the host."""
+    shape = _shape(max_seq_len=4096, kv_stride_seq=4096 * 8 * 128, split_size=256)    # 16 tiles
+    fake = ctypes.c_void_p(1 << 20)
+
+    def call(S, mode):
+        need = santa.santa_workspace_size(shape, max(S, 1), mode)
+        return lib.santa_decode_flash(ctypes.byref(shape), fake, fake, fake, fake, None, S, mode,
+                                      ctypes.c_uint64(0), fake, fake, fake, need, None)
+
+    assert call(64, 0) == UNSUPPORTED
+    assert "stratified or systematic" in lib.santa_last_error().decode()
+    assert call(15, 2) == UNSUPPORTED
+    assert "a sample for every tile" in lib.santa_last_error().decode()
+    assert call(0, 2) == INVALID
+    lay = santa.santa_workspace_layout_query(shape, 64, 2)
+    assert lay.accum_offset < lay.flash_offset < lay.records_offset
+    assert lay.records_offset - lay.flash_offset >= 256 + 32 * 16 * 130 * 8   # refs, then fp64 slots
