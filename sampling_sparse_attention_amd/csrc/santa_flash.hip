@@ -73,14 +73,15 @@ void flash_kernel(Params p) {
             hs[h].stream = 1 + it.t;
             hs[h].off = off;
         }
-        r = __shfl(r, 0, 64);
         wave_lds_sync();
         const HeadState st = hs[h];
-        // the tile's weight relative to the shared reference r, and 1/S_t
-        const double w = st.z * exp((double)st.m_t - (double)r);
-        const double scale = w / (double)n_t;
         double* slot = acc_group + ((it.t % kOutSlots) * G + h) * DA;
+        double w = 0.0;
         sample_head<G, D, E>(p, it, st, h, L, smem, [&](int col, const float* vals) {
+            // the tile's weight relative to the shared reference r, and 1/S_t; the
+            // compare-and-swap's result is first needed here, after the gather
+            w = st.z * exp((double)st.m_t - (double)__shfl(r, 0, 64));
+            const double scale = w / (double)n_t;
 #pragma unroll
             for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, scale * (double)vals[e]);
         });
