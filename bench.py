@@ -240,6 +240,23 @@ def main():
     t_step = timed(run.step, args.steps, args.eager, ncopies)
     # the two-kernel path (score pass + sample pass), for comparison
     t_two = timed(lambda c: (run.score(c), run.sample(c)), args.steps, args.eager, ncopies)
+    # S^2ANTA-flash (santa_decode_flash) on the same inputs, at this S and at the
+    # page's flash operating point S = 2048: reported beside the headline
+    flash = {}
+    if mode != W.MODE_MULTINOMIAL:
+        for S_f in sorted({S, 2048}):
+            if S_f < lay.num_splits:
+                continue
+            run_f = Runner(santa, copies, S_f, mode, args.split)
+            call = lambda c, r=run_f: santa.santa_decode_flash(*r._args(c))
+            t_f = timed(call, args.steps, args.eager, ncopies)
+            call(0)
+            torch.cuda.synchronize()
+            u_f = W.unique_v_rows(run_f.idx.cpu(), w.group)
+            b_f = W.traffic_bytes(w, copies[0]["seq_lens"].cpu().tolist(), u_f)
+            flash[f"S{S_f}"] = {"step_us": t_f * 1e6, "unique_v_rows": u_f, "algorithmic_bytes": b_f,
+                                "achieved_GBs": b_f / t_f / 1e9}
+            del run_f
 
     # algorithmic traffic of one step: all K rows + distinct sampled V rows
     lens = copies[0]["seq_lens"].cpu()
@@ -278,7 +295,7 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "bytes_per_launch": alg_bytes, "avg_launch_us": t_step * 1e6},
         "step": {"decode_us": t_step * 1e6, "decode_path": path,
-                 "two_kernel_step_us": t_two * 1e6,
+                 "two_kernel_step_us": t_two * 1e6, "flash": flash,
                  "algorithmic_bytes": alg_bytes, "k_bytes": int(lens.sum()) * w.kv_heads * w.head_dim * w.elem_bytes,
                  "unique_v_rows": uniq_mean, "dense_read_bytes": dense,
                  "dense_read_us_at_peak": dense / (PEAK_HBM_GBS * 1e9) * 1e6},
