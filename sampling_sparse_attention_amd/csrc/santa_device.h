@@ -125,6 +125,16 @@ __device__ __forceinline__ int wave_scan_max_i32(int x) {
     return x;
 }
 
+__device__ __forceinline__ int wave_scan_add_i32(int x) {
+    x += (int)dpp_u32<0x111>(0u, (uint32_t)x);
+    x += (int)dpp_u32<0x112>(0u, (uint32_t)x);
+    x += (int)dpp_u32<0x114>(0u, (uint32_t)x);
+    x += (int)dpp_u32<0x118>(0u, (uint32_t)x);
+    x += (int)dpp_u32<0x142, 0xA>(0u, (uint32_t)x);
+    x += (int)dpp_u32<0x143, 0xC>(0u, (uint32_t)x);
+    return x;
+}
+
 // The value of lane `src` (uniform) in every lane.
 __device__ __forceinline__ float lane_f32(float v, int src) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));

@@ -525,32 +525,53 @@ __device__ __forceinline__ void target_range(const Params& p, int b, int hq, dou
     }
 }
 
+// idx of the chunk's na targets from the marks of the distinct-key list: target
+// i belongs to the list entry with the largest mark at or below i (target 0 is
+// always marked); lane l scans targets [4l, 4l + 4), so every lane stores.
+__device__ __forceinline__ void write_idx_from_marks(TargetArea* ta, int na, int32_t* idx_row, int key0,
+                                                     int lane) {
+    static_assert(kTargetChunk <= 4 * 64, "four targets per lane");
+    int v[4], run = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane * 4 + k;
+        run = max(run, i < na ? ta->mark[i] : -1);
+        v[k] = run;
+    }
+    int before = __shfl_up(wave_scan_max_i32(run), 1, 64);
+    if (lane == 0) before = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = lane * 4 + k;
+        if (i < na) idx_row[i] = key0 + ta->lkey[max(before, v[k])];
+    }
+    wave_lds_sync();
+}
+
 // ---------------------------------------------------------------------------
-// Inverse-CDF sampling of targets [m0, m0 + na) of one head (one wave): each
-// target tau goes to the first key j of the split whose upper edge
-// C_{j+1} = W_t + exp(m_t - M) * P_j exceeds it (half-open intervals,
-// Appendix A.4); a target past every edge (rounding) goes to the split's last
-// key of positive mass.  Writes idx and leaves the distinct keys with their
-// sample counts, ascending, in ta->lkey / ta->lcnt; returns how many.
+// Inverse-CDF sampling of multinomial targets (the sorted uniforms)
+// [m0, m0 + na) of one head (one wave): each target tau goes to the first key
+// j of the split whose upper edge C_{j+1} = W_t + exp(m_t - M) * P_j exceeds
+// it (half-open intervals, Appendix A.4); a target past every edge (rounding)
+// goes to the split's last key of positive mass.  Writes idx and leaves the
+// distinct keys with their sample counts, ascending, in ta->lkey / ta->lcnt;
+// returns how many.
 //   few targets (<= 8): one at a time -- a ballot over the lanes' last edges
 //     (lane l owns keys [l*ept, (l+1)*ept)) finds the lane that owns the key,
 //     one LDS read per lane finds the key;
 //   more: by keys, 64 at a time (lane l takes key j0 + l): each lane counts
 //     the targets below its key's upper edge (+inf for the last key of
-//     positive mass), and the key holds the targets between that count and
-//     its left neighbour's.  For stratified and systematic targets the count
-//     is within one of a closed-form estimate (target m lies in stratum m)
-//     and is settled by one or two reads of the chunk's targets; for
-//     multinomial it is a binary search.  Every key with targets marks its
-//     first one, and a max-scan over the marks gives each target its key, so
-//     idx is written by all lanes at once.
+//     positive mass) by a binary search over the chunk's targets, and the
+//     key holds the targets between that count and its left neighbour's.
+//     Every key with targets marks its first one, and a max-scan over the
+//     marks gives each target its key, so idx is written by all lanes at once.
 // ---------------------------------------------------------------------------
-template <int MODE>
-__device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, const HeadState& st, int hq,
-                                            const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
+__device__ __forceinline__ int sample_chunk_multinomial(const Params& p, const Item& it, const HeadState& st,
+                                                        int hq, const uint64_t* ph, TargetArea* ta, int m0, int na,
+                                                        int lane) {
     const int ns = it.ns;
     int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S + m0;
-    const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0, st.n_targets, st.off, st.stream);
+    const TargetSeq<0> ts = target_seq<0>(p, it.b, hq, st.z, st.u0, st.n_targets, st.off, st.stream);
     const int lastpos = max(st.lastpos, 0);
     auto edge = [&](int j) { return st.w_lo + st.f * fixed_to_double(ph[j]); };
     if (na <= 8) {
@@ -594,7 +615,6 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
     wave_lds_sync();
     const double* tau = ta->tau;
     const int nkeys = min(ns, lastpos + 1);      // keys after lastpos take nothing
-    const double s_over_z = (double)ts.S / st.z;
     const unsigned long long below = (1ull << lane) - 1ull;
     int carry = 0;          // count below the upper edge of the key before j0
     int nlist = 0;
@@ -603,22 +623,13 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
         int c = na;
         if (j < lastpos) {
             const double u = edge(j);
-            if constexpr (MODE == 0) {
-                int lo = 0, hi = na;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (tau[mid] < u) lo = mid + 1;
-                    else hi = mid;
-                }
-                c = lo;
-            } else {
-                const double est = ts.off + (u * s_over_z - (MODE == 2 ? st.u0 : 0.0));
-                const double e = fmin(fmax(MODE == 2 ? ceil(est) : floor(est), (double)m0), (double)(m0 + na));
-                int i = (int)e - m0;
-                while (i > 0 && tau[i - 1] >= u) --i;
-                while (i < na && tau[i] < u) ++i;
-                c = i;
+            int lo = 0, hi = na;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (tau[mid] < u) lo = mid + 1;
+                else hi = mid;
             }
+            c = lo;
         }
         int first = __shfl_up(c, 1, 64);
         if (lane == 0) first = carry;
@@ -634,22 +645,202 @@ __device__ __forceinline__ int sample_chunk(const Params& p, const Item& it, con
         nlist += __popcll(bal);
     }
     wave_lds_sync();
-    // target i belongs to the list entry with the largest mark at or below i
-    // (target 0 is always marked); lane l scans targets [4l, 4l + 4)
-    int v[4], run = -1;
+    write_idx_from_marks(ta, na, idx_row, it.key0, lane);
+    return nlist;
+}
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF sampling of stratified or systematic targets [m0, m0 + na) of
+// one head (one wave), every key at once.  Target m lies in stratum m of
+// [0, Z), so the number of targets below a key's upper edge u is a closed
+// form in u (u * S / Z, less the systematic offset) up to rounding, which can
+// move it by one only where a target lies within about 1e-12 of u; one read
+// of the targets on either side settles it.  Lane l owns keys [l*ept,
+// (l+1)*ept) and counts the targets below the upper edge of each of them and
+// of key l*ept - 1, four keys at a time with their LDS reads issued together
+// (the last key of positive mass counts every target, so that targets past
+// all edges by rounding go to it).  Key j holds the targets between the count
+// of key j-1 and its own (half-open intervals, Appendix A.4) and marks the
+// first of them with its index.  Keys ascend with their targets, so a
+// max-scan over the marks gives every target its key, and the marked targets,
+// compacted in order, are the distinct keys; each holds the targets up to the
+// next mark.
+// ---------------------------------------------------------------------------
+template <int MODE>
+struct StrataCounter {
+    const uint64_t* ph;
+    const double* tau;
+    double w_lo, f, s_over_z, shift;
+    int m0, na, lastpos, last_key;
+
+    // counts for keys j[0..N) (any j; keys at or past lastpos count na)
+    template <int N>
+    __device__ __forceinline__ void operator()(const int (&j)[N], int (&c)[N]) const {
+        uint64_t pv[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) pv[q] = ph[min(max(j[q], 0), last_key)];
+        double u[N];
+        int i[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            u[q] = w_lo + f * fixed_to_double(pv[q]);
+            const double est = u[q] * s_over_z - shift;
+            const double e = fmin(fmax(MODE == 2 ? ceil(est) : floor(est), (double)m0), (double)(m0 + na));
+            i[q] = (int)e - m0;
+        }
+        double lo[N], hi[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            lo[q] = tau[max(i[q] - 1, 0)];
+            hi[q] = tau[min(i[q], na - 1)];
+        }
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+            int r = i[q];
+            if (r > 0 && lo[q] >= u[q]) r -= 1;
+            else if (r < na && hi[q] < u[q]) r += 1;
+            c[q] = j[q] >= lastpos ? na : r;
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Inverse-CDF sampling of at most 64 targets [m0, m0 + na) of one head (one
+// wave), one target per lane.  Target tau goes to the first key j of the split
+// whose upper edge W_t + exp(m_t - M) * P_j exceeds it, i.e. with P_j above
+// x = (tau - W_t) / exp(m_t - M) in the split's own fixed-point mass scale
+// (half-open intervals, Appendix A.4); a target at or past the split's total
+// (rounding) goes to the last key of positive mass.  Lane l holds P at the end
+// of its block of keys [l*ept, (l+1)*ept); a ballot per target over those block
+// ends finds the target's block, and one vector read of the block's prefix
+// finds its key.  Targets ascend with their lanes, so the distinct keys are
+// the lanes whose key differs from the lane before, compacted with a ballot;
+// each holds the targets up to the next such lane.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__device__ __forceinline__ int sample_few(const Params& p, const Item& it, const HeadState& st, int hq,
+                                          const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
+    int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S + m0;
+    const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0, st.n_targets, st.off, st.stream);
+    const int ept = p.split >> 6;
+    const bool active = lane < na;
+    // the target in the split's fixed-point scale (P_j counts 2^-52 units)
+    const double x = active ? (ts.tau(m0 + lane) - st.w_lo) / st.f * 0x1p52 : 0.0;
+    const double block_end = (double)ph[(lane + 1) * ept - 1];
+    int block = 0;
+    for (int k = 0; k < na; ++k) {
+        const double xk = lane_f64(x, k);
+        const int c = __popcll(__ballot(block_end <= xk));
+        if (lane == k) block = c;
+    }
+    const int lastpos = max(st.lastpos, 0);
+    int key = lastpos;
+    if (active && block < 64) {
+        const uint64_t* pb = ph + block * ept;
+        int below = 0;
+        for (int k = 0; k < ept; k += 2) {
+            if (ept >= 2) {
+                const ulonglong2 v2 = *reinterpret_cast<const ulonglong2*>(pb + k);
+                below += ((double)v2.x <= x ? 1 : 0) + ((double)v2.y <= x ? 1 : 0);
+            } else {
+                below += (double)pb[0] <= x ? 1 : 0;
+            }
+        }
+        key = min(block * ept + below, lastpos);
+    }
+    if (active) idx_row[lane] = it.key0 + key;
+    // distinct keys: lanes whose key differs from the previous lane's
+    int prev_key = __shfl_up(key, 1, 64);
+    const bool head = active && (lane == 0 || key != prev_key);
+    const unsigned long long heads = __ballot(head);
+    if (head) {
+        const int pos = __popcll(heads & ((1ull << lane) - 1ull));
+        const unsigned long long after = lane == 63 ? 0ull : heads & (~0ull << (lane + 1));
+        const int next = after ? __builtin_ctzll(after) : na;
+        ta->lkey[pos] = key;
+        ta->lcnt[pos] = (unsigned)(next - lane);
+    }
+    wave_lds_sync();
+    return __popcll(heads);
+}
+
+template <int MODE>
+__device__ __forceinline__ int sample_chunk_strata(const Params& p, const Item& it, const HeadState& st, int hq,
+                                                   const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
+    static_assert(MODE == 1 || MODE == 2, "stratified or systematic targets");
+    static_assert(kTargetChunk <= 4 * 64, "four targets per lane");
+    int32_t* idx_row = p.idx + ((int64_t)it.b * p.Hq + hq) * p.S + m0;
+    const TargetSeq<MODE> ts = target_seq<MODE>(p, it.b, hq, st.z, st.u0, st.n_targets, st.off, st.stream);
+    for (int k = lane; k < na; k += 64) {
+        ta->tau[k] = ts.tau(m0 + k);
+        ta->mark[k] = -1;
+    }
+    wave_lds_sync();
+    StrataCounter<MODE> cnt;
+    cnt.ph = ph;
+    cnt.tau = ta->tau;
+    cnt.w_lo = st.w_lo;
+    cnt.f = st.f;
+    cnt.s_over_z = (double)ts.S / st.z;
+    cnt.shift = (MODE == 2 ? st.u0 : 0.0) - (double)ts.off;
+    cnt.m0 = m0;
+    cnt.na = na;
+    cnt.lastpos = max(st.lastpos, 0);
+    cnt.last_key = p.split - 1;
+    const int ept = p.split >> 6;
+    const int i0 = lane * ept;
+    int prev = 0;           // count below the lower edge of the key in hand
+    for (int k0 = 0; k0 < ept; k0 += 4) {
+        int c[4];
+        const int j[4] = {i0 + k0, i0 + k0 + 1, i0 + k0 + 2, i0 + k0 + 3};
+        if (k0 == 0) {
+            // with the count below the block (key i0 - 1; none for lane 0)
+            int c5[5];
+            const int j5[5] = {i0 - 1, j[0], j[1], j[2], j[3]};
+            cnt(j5, c5);
+            prev = lane == 0 ? 0 : c5[0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c[q] = c5[q + 1];
+        } else {
+            cnt(j, c);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (k0 + q < ept && c[q] > prev) {
+                ta->mark[prev] = j[q];
+                prev = c[q];
+            }
+        }
+    }
+    wave_lds_sync();
+    // lane l: targets [4l, 4l + 4)
+    int mk[4], own[4], run = -1, nm = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int i = lane * 4 + k;
-        run = max(run, i < na ? ta->mark[i] : -1);
-        v[k] = run;
+        mk[k] = i < na ? ta->mark[i] : -1;
+        nm += mk[k] >= 0 ? 1 : 0;
+        run = max(run, mk[k]);
+        own[k] = run;
     }
     int before = __shfl_up(wave_scan_max_i32(run), 1, 64);
     if (lane == 0) before = -1;
+    const int incl = wave_scan_add_i32(nm);
+    const int nlist = lane_i32(incl, 63);
+    int pos = incl - nm;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int i = lane * 4 + k;
-        if (i < na) idx_row[i] = it.key0 + ta->lkey[max(before, v[k])];
+        if (i < na) idx_row[i] = it.key0 + max(before, own[k]);
+        if (mk[k] >= 0) {
+            ta->lkey[pos] = mk[k];
+            ta->mark[pos] = i;          // the entry's first target (marks are read above)
+            ++pos;
+        }
     }
+    wave_lds_sync();
+    for (int e = lane; e < nlist; e += 64)
+        ta->lcnt[e] = (unsigned)((e + 1 < nlist ? ta->mark[e + 1] : na) - ta->mark[e]);
     wave_lds_sync();
     return nlist;
 }
@@ -692,9 +883,11 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
     for (int m0 = st.m_lo; m0 < st.m_hi; m0 += kTargetChunk) {
         const int na = min(kTargetChunk, st.m_hi - m0);
         int nlist;
-        if (p.mode == 2) nlist = sample_chunk<2>(p, it, st, hq, ph, ta, m0, na, lane);
-        else if (p.mode == 1) nlist = sample_chunk<1>(p, it, st, hq, ph, ta, m0, na, lane);
-        else nlist = sample_chunk<0>(p, it, st, hq, ph, ta, m0, na, lane);
+        if (p.mode == 2) nlist = na <= kFewTargets ? sample_few<2>(p, it, st, hq, ph, ta, m0, na, lane)
+                                                   : sample_chunk_strata<2>(p, it, st, hq, ph, ta, m0, na, lane);
+        else if (p.mode == 1) nlist = na <= kFewTargets ? sample_few<1>(p, it, st, hq, ph, ta, m0, na, lane)
+                                                        : sample_chunk_strata<1>(p, it, st, hq, ph, ta, m0, na, lane);
+        else nlist = sample_chunk_multinomial(p, it, st, hq, ph, ta, m0, na, lane);
         for (int r0 = 0; r0 < nlist; r0 += UL * RPL) {
             uint4 x[UL];
             float wgt[UL];
