@@ -199,7 +199,7 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->split = plan->split;
     p->T = plan->T;
     p->items = (int32_t)((int64_t)s->batch * s->num_kv_heads * plan->T);
-    p->head_fastest = 0;
+    p->item_order = santa::kOrderSplitFastest;
     p->S = S;
     p->mode = mode;
     return SANTA_STATUS_OK;
@@ -243,7 +243,7 @@ santa_status run(int stages, const santa_shape* s, const void* q, const void* k,
         if (st != SANTA_STATUS_OK) return st;
     }
     if (path == 1) {
-        p.head_fastest = 1;
+        p.item_order = p.T % 8 == 0 ? santa::kOrderTokenBlocks : santa::kOrderHeadFastest;
         st = hip_check(santa::launch_fused(p, s->dtype, hs), "launching the fused decode kernel");
         if (st != SANTA_STATUS_OK) return st;
     } else {
@@ -359,7 +359,7 @@ santa_status santa_decode_flash(const santa_shape* shape, const void* q, const v
     // (sequence, KV head)-fastest: the workgroups running together read the K
     // rows of all KV heads of one range of tokens, which lie together in the
     // token-major cache (split-fastest measured 10-40 % slower)
-    p.head_fastest = 1;
+    p.item_order = santa::kOrderHeadFastest;
     st = hip_check(santa::launch_flash(p, shape->dtype, static_cast<hipStream_t>(stream)),
                    "launching the flash decode kernel");
     if (st != SANTA_STATUS_OK) return st;

@@ -77,7 +77,8 @@ void flash_kernel(Params p) {
         const HeadState st = hs[h];
         double* slot = acc_group + ((it.t % kOutSlots) * G + h) * DA;
         double w = 0.0;
-        sample_head<G, D, E>(p, it, st, h, L, smem, [&](int col, const float* vals) {
+        // two keys at a time: this kernel holds more state across the sampling
+        sample_head<G, D, E, 2>(p, it, st, h, L, smem, [&](int col, const float* vals) {
             // the tile's weight relative to the shared reference r, and 1/S_t; the
             // compare-and-swap's result is first needed here, after the gather
             w = st.z * exp((double)st.m_t - (double)__shfl(r, 0, 64));

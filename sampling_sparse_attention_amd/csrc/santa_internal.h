@@ -45,6 +45,11 @@ constexpr int kBarrierStride = 32 * kBarrierLines;   // 32-bit words per (sequen
 // word; the last split to finish sums the slots into o and clears them.
 constexpr int kOutSlots = 16;
 
+// Orders of the work items (sequence, KV head, split) over the workgroup indices.
+constexpr int kOrderSplitFastest = 0;
+constexpr int kOrderHeadFastest = 1;
+constexpr int kOrderTokenBlocks = 2;      // needs T % 8 == 0
+
 struct Params {
     const void* q;
     const void* k;
@@ -75,7 +80,7 @@ struct Params {
     int32_t split;                // keys per split, multiple of 64
     int32_t T;                    // splits per sequence: ceil(n_max / split)
     int32_t items;                // B * Hkv * T work items (one workgroup each)
-    int32_t head_fastest;         // item order: 1 (sequence, KV head)-fastest, 0 split-fastest
+    int32_t item_order;           // kOrder*: how a workgroup index maps to (b, g, t)
     int32_t S;
     int32_t mode;
 };

@@ -36,20 +36,33 @@ struct Item {
     int Tb;        // splits of sequence b
 };
 
-// Work item numbering.  The fused kernel numbers items (sequence, KV
-// head)-fastest, item = t * B * Hkv + b * Hkv + g: every group then streams its
-// splits across the whole launch, the groups reach their barriers together at
-// the end of the K stream and their latency-bound tails run side by side,
-// instead of the tails of early groups slowing the K stream of later ones
-// (with B * Hkv a multiple of 8 the splits of a group also share one XCD).
-// The two-kernel path, whose grids are larger than the device, numbers them
-// split-fastest, item = (b * Hkv + g) * T + t, so that a group's splits run
-// close together in time.
+// Work item numbering (Params::item_order).
+//   kOrderTokenBlocks (fused kernel, T a multiple of 8): workgroups are handed
+//     to the 8 XCDs round-robin by index, so item i runs on XCD i mod 8; XCD x
+//     takes the splits t = x, x + 8, ... and, for each, the B * Hkv groups one
+//     after another: item = 8 * ((t / 8) * B * Hkv + b * Hkv + g) + t mod 8.
+//     The KV heads of a token-major cache share every token row, so the
+//     workgroups reading one stretch of rows run together on one XCD and the
+//     rows are fetched together (1.4 us less K stream on the Llama-shaped
+//     step than with the order below); every group still streams across the
+//     whole launch, so the groups reach their barriers together at the end of
+//     the K stream and their latency-bound tails run side by side.
+//   kOrderHeadFastest (fused kernel otherwise, S^2ANTA-flash): item = t * B *
+//     Hkv + b * Hkv + g, with the same side-by-side tails.
+//   kOrderSplitFastest (two-kernel path, whose grids are larger than the
+//     device): item = (b * Hkv + g) * T + t, so that a group's splits run close
+//     together in time.
 __device__ __forceinline__ Item item_coords(const Params& p, int item) {
     Item it;
     int grp;
-    if (p.head_fastest) {
-        const int ng = p.B * p.Hkv;
+    const int ng = p.B * p.Hkv;
+    if (p.item_order == kOrderTokenBlocks) {
+        const int x = item & 7;
+        const int s8 = item >> 3;
+        const int tb = s8 / ng;
+        it.t = 8 * tb + x;
+        grp = s8 - tb * ng;
+    } else if (p.item_order == kOrderHeadFastest) {
         it.t = item / ng;
         grp = item - it.t * ng;
     } else {
@@ -174,12 +187,13 @@ struct ScoreStream {
     static constexpr int M = NVP / LPR;
     static_assert(LPR >= 2 && LPR <= 32 && 16 % RPL == 0, "row shape");
 
-    // Loads of the CB chunks base, base + NW, ... (16 rows each).
+    // Loads of the NC chunks base, base + NW, ... (16 rows each).
+    template <int NC>
     __device__ __forceinline__ static void issue(const Params& p, const Item& it, const int* pages,
                                                  const char* kbase, int64_t first, int base, int nchunks,
-                                                 int c, int li, uint4 (&kd)[CB][R]) {
+                                                 int c, int li, uint4 (&kd)[NC][R]) {
 #pragma unroll
-        for (int k = 0; k < CB; ++k) {
+        for (int k = 0; k < NC; ++k) {
             const int ch = base + k * NW;
             const int r0 = ch << 4;
             // a 16-row chunk never straddles a page (pages >= 16 rows, r0 % 16 == 0)
@@ -194,11 +208,12 @@ struct ScoreStream {
         }
     }
 
+    template <int NC>
     __device__ __forceinline__ static void score(const Params& p, const Item& it, float* sc, int base,
                                                  int nchunks, int c, int li, const uint4 (&qf)[G],
-                                                 const uint4 (&kd)[CB][R]) {
+                                                 const uint4 (&kd)[NC][R]) {
 #pragma unroll
-        for (int k = 0; k < CB; ++k) {
+        for (int k = 0; k < NC; ++k) {
             const int ch = base + k * NW;
             if (ch < nchunks) {
                 float acc[NVP];
@@ -250,11 +265,11 @@ __device__ __forceinline__ void stream_scores(const Params& p, const Item& it, f
     const int64_t first = row_offset(p, it, 0, pages);
 
     uint4 kd[SS::CB][SS::R];
-    SS::issue(p, it, pages, kbase, first, wave, nchunks, c, li, kd);
-    SS::score(p, it, sc, wave, nchunks, c, li, qf, kd);
+    SS::template issue<SS::CB>(p, it, pages, kbase, first, wave, nchunks, c, li, kd);
+    SS::template score<SS::CB>(p, it, sc, wave, nchunks, c, li, qf, kd);
     for (int base = wave + SS::NW * SS::CB; base < nchunks; base += SS::NW * SS::CB) {
-        SS::issue(p, it, pages, kbase, first, base, nchunks, c, li, kd);
-        SS::score(p, it, sc, base, nchunks, c, li, qf, kd);
+        SS::template issue<SS::CB>(p, it, pages, kbase, first, base, nchunks, c, li, kd);
+        SS::template score<SS::CB>(p, it, sc, base, nchunks, c, li, qf, kd);
     }
 }
 
@@ -657,7 +672,7 @@ __device__ __forceinline__ int sample_chunk_multinomial(const Params& p, const I
 // move it by one only where a target lies within about 1e-12 of u; one read
 // of the targets on either side settles it.  Lane l owns keys [l*ept,
 // (l+1)*ept) and counts the targets below the upper edge of each of them and
-// of key l*ept - 1, four keys at a time with their LDS reads issued together
+// of key l*ept - 1, KW keys at a time with their LDS reads issued together
 // (the last key of positive mass counts every target, so that targets past
 // all edges by rounding go to it).  Key j holds the targets between the count
 // of key j-1 and its own (half-open intervals, Appendix A.4) and marks the
@@ -764,7 +779,7 @@ __device__ __forceinline__ int sample_few(const Params& p, const Item& it, const
     return __popcll(heads);
 }
 
-template <int MODE>
+template <int MODE, int KW>
 __device__ __forceinline__ int sample_chunk_strata(const Params& p, const Item& it, const HeadState& st, int hq,
                                                    const uint64_t* ph, TargetArea* ta, int m0, int na, int lane) {
     static_assert(MODE == 1 || MODE == 2, "stratified or systematic targets");
@@ -789,23 +804,20 @@ __device__ __forceinline__ int sample_chunk_strata(const Params& p, const Item& 
     cnt.last_key = p.split - 1;
     const int ept = p.split >> 6;
     const int i0 = lane * ept;
-    int prev = 0;           // count below the lower edge of the key in hand
-    for (int k0 = 0; k0 < ept; k0 += 4) {
-        int c[4];
-        const int j[4] = {i0 + k0, i0 + k0 + 1, i0 + k0 + 2, i0 + k0 + 3};
-        if (k0 == 0) {
-            // with the count below the block (key i0 - 1; none for lane 0)
-            int c5[5];
-            const int j5[5] = {i0 - 1, j[0], j[1], j[2], j[3]};
-            cnt(j5, c5);
-            prev = lane == 0 ? 0 : c5[0];
+    int prev;               // count below the lower edge of the key in hand
+    {
+        int c1[1];
+        const int j1[1] = {i0 - 1};     // the count below the block (none for lane 0)
+        cnt(j1, c1);
+        prev = lane == 0 ? 0 : c1[0];
+    }
+    for (int k0 = 0; k0 < ept; k0 += KW) {
+        int c[KW], j[KW];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) c[q] = c5[q + 1];
-        } else {
-            cnt(j, c);
-        }
+        for (int q = 0; q < KW; ++q) j[q] = i0 + k0 + q;
+        cnt(j, c);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < KW; ++q) {
             if (k0 + q < ept && c[q] > prev) {
                 ta->mark[prev] = j[q];
                 prev = c[q];
@@ -858,7 +870,9 @@ __device__ __forceinline__ int sample_chunk_strata(const Params& p, const Item& 
 // The head's sum of count-weighted rows goes to emit(col, vals): every lane
 // passes D/64 consecutive elements starting at column col, and the 64 lanes
 // cover the row once.
-template <int G, int D, typename E, typename Emit>
+// KW: keys whose target counts the stratified/systematic sampler evaluates at
+// once (more overlaps more LDS reads, at the cost of registers).
+template <int G, int D, typename E, int KW = 4, typename Emit>
 __device__ __forceinline__ void sample_head(const Params& p, const Item& it, const HeadState& st, int h,
                                             const LdsLayout& L, unsigned char* smem, Emit&& emit) {
     constexpr int LPR = D * E::bytes / 16;      // lanes per V row
@@ -884,9 +898,9 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
         const int na = min(kTargetChunk, st.m_hi - m0);
         int nlist;
         if (p.mode == 2) nlist = na <= kFewTargets ? sample_few<2>(p, it, st, hq, ph, ta, m0, na, lane)
-                                                   : sample_chunk_strata<2>(p, it, st, hq, ph, ta, m0, na, lane);
+                                                   : sample_chunk_strata<2, KW>(p, it, st, hq, ph, ta, m0, na, lane);
         else if (p.mode == 1) nlist = na <= kFewTargets ? sample_few<1>(p, it, st, hq, ph, ta, m0, na, lane)
-                                                        : sample_chunk_strata<1>(p, it, st, hq, ph, ta, m0, na, lane);
+                                                        : sample_chunk_strata<1, KW>(p, it, st, hq, ph, ta, m0, na, lane);
         else nlist = sample_chunk_multinomial(p, it, st, hq, ph, ta, m0, na, lane);
         for (int r0 = 0; r0 < nlist; r0 += UL * RPL) {
             uint4 x[UL];
