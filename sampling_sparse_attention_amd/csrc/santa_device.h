@@ -218,8 +218,17 @@ __device__ __forceinline__ float mass_exp(float x) { return __expf(x); }
 // Masses inside a split are summed as 52-bit fixed point (e <= 1, so a split
 // of <= 1024 keys stays below 2^62): integer sums are exact and independent of
 // their order, so the prefix sums P_i are exactly non-decreasing and their
-// last value is the split's total.
-__device__ __forceinline__ uint64_t fixed_mass(float e) { return (uint64_t)(e * 0x1p52f); }
+// last value is the split's total.  Conversions to fixed point round to
+// nearest: for x * scale in [0, 2^52] (exact, scale a power of two), adding
+// 2^52 in one FMA leaves the rounded integer in the low bits of the double
+// (instead of the library's multi-step double-to-integer sequence).
+__device__ __forceinline__ uint64_t fixed_round(double x, double scale) {
+    return (uint64_t)__double_as_longlong(fma(x, scale, 0x1p52)) - 0x4330000000000000ull;
+}
+__device__ __forceinline__ uint64_t fixed_mass(float e) { return fixed_round((double)e, 0x1p52); }
+// A split's mass w <= 1024 on the 2^-40 grid of the cross-split prefix
+// (w * 2^40 < 2^52).
+__device__ __forceinline__ uint64_t fixed40(double w) { return fixed_round(w, 0x1p40); }
 __device__ __forceinline__ double fixed_to_double(uint64_t v) { return (double)v * 0x1p-52; }
 
 // ---------------------------------------------------------------------------

@@ -955,7 +955,9 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int Tb = it.Tb;
-    const int K = (Tb + 63) >> 6;               // records per lane, <= kRecPerLane
+    // records per lane: the power of two K = 2^ks with 64 K >= Tb (K <= kRecPerLane)
+    const int ks = Tb <= 64 ? 0 : Tb <= 128 ? 1 : Tb <= 256 ? 2 : 3;
+    const int K = 1 << ks;
     bool ok_all = true;
     for (int h = wave; h < G; h += NW) {
         const int hq = it.g * G + h;
@@ -1008,8 +1010,8 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
         const float M = wave_max_f32(mx);
         // lane-local exclusive prefix at the positions of splits t and t + 1
         const int t = it.t;
-        const int kt = t % K;
-        const int kt1 = (t + 1) % K;
+        const int kt = t & (K - 1);
+        const int kt1 = (t + 1) & (K - 1);
         uint64_t run = 0, at_t = 0, at_t1 = 0;
         int last = -1;
 #pragma unroll
@@ -1018,7 +1020,7 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
             uint64_t w = 0;
             if (k < K && j < Tb) {
                 const double f = (double)mass_exp(mr[k] - M);
-                w = (uint64_t)((double)lr[k] * f * 0x1p40);
+                w = fixed40((double)lr[k] * f);
                 if (w) last = j;
             }
             if (k == kt) at_t = run;
@@ -1032,8 +1034,8 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
         // W_t and W_{t+1} (exclusive prefixes of splits t and t+1)
         const uint64_t mine_t = excl + at_t;
         const uint64_t mine_t1 = excl + at_t1;
-        const uint64_t W_t = lane_u64(mine_t, t / K);
-        const uint64_t W_t1 = (t + 1 < Tb) ? lane_u64(mine_t1, (t + 1) / K) : Z;
+        const uint64_t W_t = lane_u64(mine_t, t >> ks);
+        const uint64_t W_t1 = (t + 1 < Tb) ? lane_u64(mine_t1, (t + 1) >> ks) : Z;
 
         const double u0 = hs[h].u0;
         const double z = (double)Z * 0x1p-40;
