@@ -182,6 +182,7 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->stash_row = (int64_t)plan->T * plan->split;
     p->seed = seed;
     p->scale = (float)(1.0 / __builtin_sqrt((double)s->head_dim));
+    p->inv_S = 1.0 / (double)S;
     p->B = s->batch;
     p->Hq = s->num_q_heads;
     p->Hkv = s->num_kv_heads;

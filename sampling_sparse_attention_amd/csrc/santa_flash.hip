@@ -65,6 +65,7 @@ void flash_kernel(Params p) {
             const double z = fixed_to_double(prefix[h * p.split + it.ns - 1]);
             hs[h].w_lo = 0.0;
             hs[h].f = 1.0;
+            hs[h].inv_f = 1.0;
             hs[h].z = z;
             hs[h].u0 = p.mode == 2 ? uniform01(p.seed, it.b, hq, 0ull, (uint64_t)(1 + it.t)) : 0.0;
             hs[h].m_lo = off;
@@ -77,8 +78,9 @@ void flash_kernel(Params p) {
         const HeadState st = hs[h];
         double* slot = acc_group + ((it.t % kOutSlots) * G + h) * DA;
         double w = 0.0;
-        // two keys at a time: this kernel holds more state across the sampling
-        sample_head<G, D, E, 2>(p, it, st, h, L, smem, [&](int col, const float* vals) {
+        // two keys at a time and four V loads per lane in flight: this kernel holds
+        // more state across the sampling, and a tile samples few rows
+        sample_head<G, D, E, 2, 4>(p, it, st, h, L, smem, [&](int col, const float* vals) {
             // the tile's weight relative to the shared reference r, and 1/S_t; the
             // compare-and-swap's result is first needed here, after the gather
             w = st.z * exp((double)st.m_t - (double)__shfl(r, 0, 64));

@@ -71,6 +71,7 @@ struct Params {
     int64_t stride_head;
     int64_t stash_row;            // floats per (b, h) row of the stash (T * split)
     uint64_t seed;
+    double inv_S;                 // 1 / S
     float scale;                  // 1 / sqrt(d)
     int32_t B, Hq, Hkv, G, D;
     int32_t n_max;

@@ -88,6 +88,7 @@ struct HeadState {
     double w_lo;    // mass of the sequence's splits before this one (W_t)
     double z;       // total mass Z of the sequence
     double f;       // exp(m_t - M)
+    double inv_f;   // exp(M - m_t), the split's scale back to its own masses
     double u0;      // systematic offset
     float m_t;      // this split's maximum score
     float l_t;      // this split's mass, sum of exp(s_i - m_t)
@@ -442,6 +443,7 @@ struct TargetSeq {
     const double* sorted;
     double u0;
     double z;
+    double inv_s;   // 1 / S, rounded once
     uint64_t seed;
     int S, off, stream, b, hq;
     __device__ __forceinline__ double tau(int m) const {
@@ -450,9 +452,9 @@ struct TargetSeq {
         if constexpr (MODE == 0) {
             t = sorted[m];
         } else if constexpr (MODE == 1) {
-            t = ((double)j + uniform01(seed, b, hq, (uint64_t)j, (uint64_t)stream)) / (double)S;
+            t = ((double)j + uniform01(seed, b, hq, (uint64_t)j, (uint64_t)stream)) * inv_s;
         } else {
-            t = ((double)j + u0) / (double)S;
+            t = ((double)j + u0) * inv_s;
         }
         return t * z;
     }
@@ -494,6 +496,7 @@ __device__ __forceinline__ TargetSeq<MODE> target_seq(const Params& p, int b, in
     ts.sorted = p.targets + ((int64_t)b * p.Hq + hq) * p.S;
     ts.seed = p.seed;
     ts.S = n_targets < 0 ? p.S : n_targets;
+    ts.inv_s = n_targets < 0 ? p.inv_S : 1.0 / (double)n_targets;
     ts.off = off;
     ts.stream = stream;
     ts.b = b;
@@ -520,7 +523,8 @@ __device__ __forceinline__ void target_range(const Params& p, int b, int hq, dou
     } else {
         const bool upper = lane >= 32;
         const double x = upper ? w_hi : w_lo;
-        const double est = x / z * (double)p.S - (MODE == 2 ? u0 : 0.0);
+        // an estimate within far less than one target of the count: a fast reciprocal will do
+        const double est = x * ((double)p.S * (double)__builtin_amdgcn_rcpf((float)z)) - (MODE == 2 ? u0 : 0.0);
         const int base = (int)ceil(fmin(fmax(est, -1.0), (double)p.S)) - 16;
         const int m = base + (lane & 31);
         // targets below index 0 do not exist: count them as below x, so that
@@ -740,7 +744,7 @@ __device__ __forceinline__ int sample_few(const Params& p, const Item& it, const
     const int ept = p.split >> 6;
     const bool active = lane < na;
     // the target in the split's fixed-point scale (P_j counts 2^-52 units)
-    const double x = active ? (ts.tau(m0 + lane) - st.w_lo) / st.f * 0x1p52 : 0.0;
+    const double x = active ? (ts.tau(m0 + lane) - st.w_lo) * st.inv_f * 0x1p52 : 0.0;
     const double block_end = (double)ph[(lane + 1) * ept - 1];
     int block = 0;
     for (int k = 0; k < na; ++k) {
@@ -871,14 +875,14 @@ __device__ __forceinline__ int sample_chunk_strata(const Params& p, const Item& 
 // passes D/64 consecutive elements starting at column col, and the 64 lanes
 // cover the row once.
 // KW: keys whose target counts the stratified/systematic sampler evaluates at
-// once (more overlaps more LDS reads, at the cost of registers).
-template <int G, int D, typename E, int KW = 4, typename Emit>
+// once; UL: V loads in flight per lane (more overlaps more memory accesses, at
+// the cost of registers).
+template <int G, int D, typename E, int KW = 4, int UL = 8, typename Emit>
 __device__ __forceinline__ void sample_head(const Params& p, const Item& it, const HeadState& st, int h,
                                             const LdsLayout& L, unsigned char* smem, Emit&& emit) {
     constexpr int LPR = D * E::bytes / 16;      // lanes per V row
     constexpr int RPL = 64 / LPR;               // rows per wave-wide load
     constexpr int ELV = 16 / E::bytes;          // elements per lane per row
-    constexpr int UL = 8;                       // loads in flight per lane
     constexpr int EL = D / 64;                  // output elements added per lane
     static_assert(RPL * LPR == 64 && ELV == EL * RPL, "row shape");
     const int lane = threadIdx.x & 63;
@@ -1045,18 +1049,17 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
         if (p.mode == 2) target_range<2>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
         else if (p.mode == 1) target_range<1>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
         else target_range<0>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
-        if (lane == 0) {
-            hs[h].w_lo = w_lo;
-            hs[h].z = z;
-            hs[h].f = (double)mass_exp(hs[h].m_t - M);
-            hs[h].m_lo = m_lo;
-            hs[h].m_hi = max(m_hi, m_lo);
-            hs[h].n_targets = p.S;
-            hs[h].stream = 0;
-            hs[h].off = 0;
-        }
-        wave_lds_sync();
-        const HeadState st = hs[h];
+        // the head's state in registers (every value here is the same in all lanes)
+        HeadState st = hs[h];
+        st.w_lo = w_lo;
+        st.z = z;
+        st.f = (double)mass_exp(st.m_t - M);
+        st.inv_f = (double)mass_exp(M - st.m_t);
+        st.m_lo = m_lo;
+        st.m_hi = max(m_hi, m_lo);
+        st.n_targets = p.S;
+        st.stream = 0;
+        st.off = 0;
         if (st.m_hi > st.m_lo) {
             // into accumulation slot t mod 16 of the group
             float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D;
