@@ -8,8 +8,11 @@
 
 namespace santa {
 
+// Four workgroups per CU where that fits without spilling registers: the pass is
+// bound by the latency of each workgroup's chain of steps, so residency is speed.
 template <int G, int D, typename E, int NT>
-__global__ __launch_bounds__(NT) void sample_kernel(Params p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
+void sample_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Item it = make_item(p, blockIdx.x);
     if (it.n == 0) {
