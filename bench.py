@@ -8,6 +8,10 @@ samples.  ``--kv-copies`` independent caches (default 8, 1 GiB) are cycled
 through, one per step like the layers of a model, so that K is read from HBM
 and not from the 256 MB Infinity Cache.
 
+The timed steps are graph replays split into 10 rounds; the line reports the mean
+over all of them as the value and, beside it, the median of the round means with
+a 95 % bootstrap interval.
+
 Prints one JSON line: throughput in heads x batch per second, the roofline of
 the dominant kernel (the fused decode kernel, bound by HBM bandwidth: all of K
 plus the distinct sampled V rows per launch), the two-kernel path's stage
@@ -162,13 +166,37 @@ def timed(fn, reps, eager, ncopies):
     replays = max(1, reps // per_graph)
     graph.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(replays):
-        graph.replay()
-    end.record(stream)
+    # events at round boundaries (ROUNDS rounds of about equal length) on the
+    # launch stream; the whole interval gives the mean, the rounds its spread
+    nr = min(ROUNDS, replays)
+    marks = [round(i * replays / nr) for i in range(nr + 1)]
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(nr + 1)]
+    events[0].record(stream)
+    for r in range(nr):
+        for _ in range(marks[r + 1] - marks[r]):
+            graph.replay()
+        events[r + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / (replays * per_graph) * 1e-3
+    LAST_ROUNDS[:] = [events[r].elapsed_time(events[r + 1]) / ((marks[r + 1] - marks[r]) * per_graph) * 1e-3
+                      for r in range(nr)]
+    return events[0].elapsed_time(events[-1]) / (replays * per_graph) * 1e-3
+
+
+ROUNDS = 10
+LAST_ROUNDS = []        # seconds per call in each round of the last graph-timed call of timed()
+
+
+def round_stats(rounds, seed=0, n_boot=2000):
+    """Median of the per-round times and a 95 % bootstrap interval of it (seconds)."""
+    import numpy as np
+    x = np.asarray(rounds, dtype=np.float64)
+    if x.size == 0:
+        return None
+    rng = np.random.default_rng(seed)
+    boot = np.median(x[rng.integers(0, x.size, size=(n_boot, x.size))], axis=1)
+    return {"rounds": int(x.size), "median_us": float(np.median(x)) * 1e6,
+            "ci95_us": [float(np.percentile(boot, 2.5)) * 1e6, float(np.percentile(boot, 97.5)) * 1e6],
+            "min_us": float(x.min()) * 1e6, "max_us": float(x.max()) * 1e6}
 
 
 def cpu_baseline(w, x_gpu, S, mode, seconds):
@@ -238,6 +266,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] timing steps", file=sys.stderr, flush=True)
     t_step = timed(run.step, args.steps, args.eager, ncopies)
+    step_rounds = None if args.eager else round_stats(LAST_ROUNDS)
     # the two-kernel path (score pass + sample pass), for comparison
     t_two = timed(lambda c: (run.score(c), run.sample(c)), args.steps, args.eager, ncopies)
     # S^2ANTA-flash (santa_decode_flash) on the same inputs, at this S and at the
@@ -294,7 +323,7 @@ def main():
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "bytes_per_launch": alg_bytes, "avg_launch_us": t_step * 1e6},
-        "step": {"decode_us": t_step * 1e6, "decode_path": path,
+        "step": {"decode_us": t_step * 1e6, "decode_rounds": step_rounds, "decode_path": path,
                  "two_kernel_step_us": t_two * 1e6, "flash": flash,
                  "algorithmic_bytes": alg_bytes, "k_bytes": int(lens.sum()) * w.kv_heads * w.head_dim * w.elem_bytes,
                  "unique_v_rows": uniq_mean, "dense_read_bytes": dense,
