@@ -44,6 +44,20 @@ def test_decode_small_bf16_gqa4(mode, S):
     print(rep)
 
 
+@pytest.mark.parametrize("per_split", [31, 32, 33, 64])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_sampler_paths_at_the_few_target_limit(per_split, mode):
+    """q = 0 makes every score 0, so the 2048 keys have equal mass and the
+    stratified or systematic targets fall evenly: S = 4 * per_split puts
+    exactly per_split of them into each of the four 512-key splits.  Up to 32
+    targets a split places one target per lane, above that it counts targets
+    per key; both must reproduce the oracle's indices."""
+    x = _inputs(lens=(2048,), q_scale=0.0, sinks=0)
+    S = 4 * per_split
+    o, idx, _, _ = H.run_hip(x, S, mode, seed=7, split=512)
+    print(H.check_all(x, S, mode, 7, o, idx))
+
+
 @pytest.mark.parametrize("split", [64, 128, 512, 1024])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_decode_split_sizes(split, mode):
