@@ -40,11 +40,26 @@ METRIC = "decode attention steps/sec (heads×batch) at 32k ctx; achieved HBM GB/
 KERNEL_SOURCES = ["santa_fused.hip", "santa_split.h", "santa_device.h", "santa_internal.h"]
 
 
-def kernel_source_hash() -> str:
+def strip_comments(text: str) -> str:
+    """C/C++ source without its comments and blank lines (string literals in these
+    sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the fused kernel's sources, comments left out (a comment edit
+    does not change the kernel the counters were taken on)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sampling_sparse_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, "sampling_sparse_attention_amd", "csrc", name)) as f:
+                text = f.read()
+        else:
+            text = read(name)
+        h.update(strip_comments(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -12,7 +12,7 @@ constexpr int kRecPerLane = 8;           // split records per lane when a wave m
 constexpr int kMaxSplitsPerSeq = 64 * kRecPerLane;   // T: splits of one sequence
 constexpr int kMaxSamples = 65535;
 constexpr int kMaxSortSamples = 8192;
-constexpr int kTargetChunk = 256;        // targets per merge-path pass of one wave
+constexpr int kTargetChunk = 256;        // targets one wave places per pass
 constexpr int kFewTargets = 32;          // up to this many targets of a chunk: one target per lane
 constexpr int kSpinLimit = 1 << 21;      // polls of a bounded wait (about 1 us each)
 

@@ -18,9 +18,9 @@
 //                  prefix W of split masses and the total Z (the global
 //                  partition function of section 3.2, step 2) and the range of
 //                  targets this split owns, then samples them by inverse CDF
-//                  (section 2.1 and Appendix A.4) with a merge path against
-//                  the split's CDF and gathers-and-adds the sampled V rows
-//                  with duplicates counted (section 2, Eq. 2-3).
+//                  (section 2.1 and Appendix A.4), merging the sorted targets
+//                  with the split's sorted CDF edges, and gathers-and-adds the
+//                  sampled V rows with duplicates counted (section 2, Eq. 2-3).
 #pragma once
 
 #include "santa_device.h"
