@@ -113,7 +113,9 @@ struct LdsLayout {
 // Per wave, for one chunk of at most kTargetChunk targets of one head.
 struct TargetArea {
     double tau[kTargetChunk];      // targets scaled by Z
-    int mark[kTargetChunk];        // list entry whose first target this is, else -1
+    int mark[kTargetChunk];        // per target: the list entry (multinomial) or the key
+                                   // (stratified/systematic) whose first target it is, else
+                                   // -1; the latter then holds each entry's first target
     int lkey[kTargetChunk];        // distinct sampled keys, ascending
     unsigned int lcnt[kTargetChunk];   // samples of each of them
 };
