@@ -44,6 +44,16 @@ def test_decode_small_bf16_gqa4(mode, S):
     print(rep)
 
 
+@pytest.mark.parametrize("mode,S", [(0, 8192), (1, 65535), (2, 65535)])
+def test_maximum_sample_counts(mode, S):
+    """The largest S each rule is built for (8192 sorted multinomial targets,
+    65535 stratified or systematic ones): thousands of targets per split, placed
+    in chunks of 256, and idx rows of S entries."""
+    x = _inputs(lens=(3000, 1200))
+    o, idx, _, _ = H.run_hip(x, S, mode, seed=13)
+    print(H.check_all(x, S, mode, 13, o, idx))
+
+
 @pytest.mark.parametrize("per_split", [31, 32, 33, 64])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_sampler_paths_at_the_few_target_limit(per_split, mode):
