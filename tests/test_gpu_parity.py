@@ -44,6 +44,23 @@ def test_decode_small_bf16_gqa4(mode, S):
     print(rep)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_many_splits_per_sequence(mode):
+    """64-key splits over sequences of 101 and 301 splits: the cross-split merge
+    then holds two and eight split records per lane (one and four are covered by
+    the 32k and 128k workloads)."""
+    # two sequences: 1204 work items, more than the device holds at once (two-kernel path)
+    x = _inputs(lens=(64 * 100 + 37, 64 * 300 + 5))
+    o, idx, _, _ = H.run_hip(x, 300, mode, seed=17, split=64)
+    print(H.check_all(x, 300, mode, 17, o, idx))
+    # one sequence of 301 splits: 602 work items (fused kernel)
+    x = _inputs(lens=(64 * 300 + 5,))
+    shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len, split_size=64)
+    assert santa.santa_decode_path(shape, 300, mode) == santa.PATH_FUSED
+    o, idx, _, _ = H.run_hip(x, 300, mode, seed=17, split=64)
+    print(H.check_all(x, 300, mode, 17, o, idx))
+
+
 @pytest.mark.parametrize("mode,S", [(0, 8192), (1, 65535), (2, 65535)])
 def test_maximum_sample_counts(mode, S):
     """The largest S each rule is built for (8192 sorted multinomial targets,
