@@ -48,6 +48,19 @@ __device__ __forceinline__ double uniform01(uint64_t seed, int b, int h, uint64_
 }
 
 // ---------------------------------------------------------------------------
+// Wave priority (fused kernel).  A workgroup streaming K issues ahead of a
+// co-resident one that has finished its stream and runs its tail (statistics,
+// merge, sampling), so the scoring between two batches of K loads, and with it
+// the next batch, is not held up behind tail arithmetic: the last K stream of
+// the Llama-shaped step ends about 0.5 us earlier.  Grids larger than the
+// device (two-kernel path, flash) gain nothing or lose: there a finished tail
+// frees its slot for the next workgroup.  Lowering the priority where it was
+// never raised does nothing.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void priority_streaming() { __builtin_amdgcn_s_setprio(2); }
+__device__ __forceinline__ void priority_tail() { __builtin_amdgcn_s_setprio(0); }
+
+// ---------------------------------------------------------------------------
 // Cross-lane data movement with DPP (VALU-only, no LDS traffic).
 //
 // dpp<CTRL, ROWS>(identity, v): v taken from the lane CTRL names, or

@@ -46,6 +46,7 @@ void fused_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Item at = item_coords(p, blockIdx.x);
     uint4 qf[G];
+    priority_streaming();
     load_q<G, D, E, NT>(p, at.b, at.g, qf);
     fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), qf, smem);
 }

@@ -274,6 +274,7 @@ __device__ __forceinline__ void stream_scores(const Params& p, const Item& it, f
         SS::template issue<SS::CB>(p, it, pages, kbase, first, base, nchunks, c, li, kd);
         SS::template score<SS::CB>(p, it, sc, base, nchunks, c, li, qf, kd);
     }
+    priority_tail();
 }
 
 // Record of split t of query head hq of sequence b: one 64-bit word
