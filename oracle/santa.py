@@ -180,8 +180,14 @@ def estimate(values: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 
 def boundary_distance(F: np.ndarray, idx: np.ndarray, t: np.ndarray) -> np.ndarray:
-    """Distance of each target from the nearer edge of the interval it fell in."""
-    return np.minimum(t - F[idx], F[idx + 1] - t)
+    """Distance of each target ``t`` from the nearer edge of the interval
+    ``[F[idx], F[idx+1])`` of the key it selected (Appendix A.4's half-open
+    intervals): ``min(|t - F[idx]|, |F[idx+1] - t|)``.  A target that rounded to
+    ``t >= F[n]`` (reading 4) lies past the upper edge of the last key of
+    positive mass, so its distance is ``t - F[idx+1] >= 0``, not negative."""
+    F = np.asarray(F, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    return np.minimum(np.abs(t - F[idx]), np.abs(F[idx + 1] - t))
 
 
 def sample_head(s: np.ndarray, S: int, mode: int, seed: int, b: int, h: int):
@@ -280,41 +286,6 @@ def estimate_flash(values: np.ndarray, idx: np.ndarray, tile_of: np.ndarray, bud
         rows = values[np.asarray(idx)[tile_of == t]]
         o += weight[t] * rows.sum(axis=0) / budget[t]
     return o
-
-
-def decode_flash(q, k_cache, v_cache, seq_lens, block_table, page_size, S, mode, seed, tile,
-                 heads=None):
-    """S^2ANTA-flash decode for a batch of single-token queries; arguments as in
-    :func:`decode` plus the tile size.  Returns per-(b, h) dicts with ``o``,
-    ``idx`` (``[S]``), ``t``, ``delta``, ``tile_of`` and ``n``."""
-    q = np.asarray(q, dtype=np.float64)
-    B, Hq, d = q.shape
-    Hkv = k_cache.shape[2]
-    G = Hq // Hkv
-    if heads is None:
-        heads = [(b, h) for b in range(B) for h in range(Hq)]
-    out = {}
-    rows_cache = {}
-    for b, h in heads:
-        n = int(seq_lens[b])
-        g = h // G
-        if n == 0:
-            out[(b, h)] = dict(o=np.zeros(d), idx=np.full(S, -1, dtype=np.int64), t=None,
-                               delta=None, tile_of=None, n=0)
-            continue
-        if (b, g) not in rows_cache:
-            rows_cache.clear()
-            keys = sequence_keys(k_cache, n, b, block_table, page_size)[:, g, :]
-            vals = sequence_keys(v_cache, n, b, block_table, page_size)[:, g, :]
-            rows_cache[(b, g)] = (np.asarray(keys, np.float64), np.asarray(vals, np.float64))
-        keys, vals = rows_cache[(b, g)]
-        s = scores(q[b, h], keys)
-        r = sample_head_flash(s, S, mode, seed, b, h, tile)
-        r["o"] = estimate_flash(vals, r["idx"], r["tile_of"], r["budget"], r["weight"])
-        r["n"] = n
-        r["s"] = s
-        out[(b, h)] = r
-    return out
 
 
 def decode(q, k_cache, v_cache, seq_lens, block_table, page_size, S, mode, seed,

@@ -1,5 +1,6 @@
 """santa_decode_flash (S^2ANTA-flash, section 3.3 of the SANTA page) against the
-oracle's decode_flash: small seeded inputs spanning several tiles and ragged
+oracle's per-head flash sampling (sample_head_flash) and deferred-normalisation
+merge (estimate_flash), both pinned on the CPU: small seeded inputs spanning several tiles and ragged
 tails, every rule and shape the kernel is built for, budgets from one sample per
 tile to several chunks of 256 per tile, and the workloads at full size (sampled
 heads).  Every call goes through the C ABI."""

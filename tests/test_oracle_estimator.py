@@ -211,6 +211,29 @@ def test_empty_sequence_gives_zero_and_minus_one():
         assert res[(0, h)]["idx"].min() >= 0
 
 
+def test_boundary_distance_on_hand_built_cdf():
+    """Appendix A.4: key j owns the half-open interval [F(j), F(j+1)); the
+    distance of a target is to the nearer edge of its key's interval.  Dyadic
+    CDF and targets, so every expected distance is exact."""
+    p = np.array([0.25, 0.25, 0.0, 0.5])
+    F = O.cdf(p)                                 # 0, 1/4, 1/2, 1/2, 1
+    eps = 2.0 ** -30
+    t = np.array([
+        0.5 - eps,          # just below the upper edge of key 1
+        0.25 + eps,         # just above the lower edge of key 1
+        0.25,               # exactly on the lower edge of key 1 (half-open: key 1)
+        0.375,              # middle of key 1
+        0.5,                # lower edge of key 3 (key 2 has no mass)
+        0.75 + eps,         # inside key 3, nearer its upper edge (by 1/4 - eps)
+        1.0 - eps,          # just below F(n)
+        1.0 + 2.0 ** -40,   # rounded past F(n): clamps to key 3
+    ])
+    idx = O.inverse_cdf(F, p, t)
+    assert idx.tolist() == [1, 1, 1, 1, 3, 3, 3, 3]
+    want = [eps, eps, 0.0, 0.125, 0.0, 0.25 - eps, eps, 2.0 ** -40]
+    assert O.boundary_distance(F, idx, t).tolist() == want
+
+
 def test_boundary_distance_is_nonnegative_and_small_for_flat_law():
     rng = np.random.default_rng(10)
     s = rng.standard_normal(4096)

@@ -14,7 +14,7 @@ from tests import test_oracle_rng as R
 
 _orig = {name: getattr(O, name) for name in
          ("scores", "cdf", "inverse_cdf", "targets_from_uniforms", "estimate", "uniforms",
-          "sequence_keys", "softmax")}
+          "sequence_keys", "softmax", "boundary_distance")}
 
 
 def _toy():
@@ -69,6 +69,11 @@ MUTATIONS = {
         (np.asarray(j, np.uint64), np.uint64(h), np.uint64(b), np.uint64(0)), (seed, 0))[0]
         & np.uint64((1 << 53) - 1)).astype(np.float64) * 2.0 ** -53),
     "softmax_no_normalise": ("softmax", lambda s: np.exp(np.asarray(s) - np.max(s))),
+    "boundary_distance_zero": ("boundary_distance", lambda F, idx, t: np.zeros(len(t))),
+    "boundary_distance_lower_edge_only": ("boundary_distance", lambda F, idx, t: np.asarray(t) - F[idx]),
+    "boundary_distance_upper_edge_only": ("boundary_distance", lambda F, idx, t: F[idx + 1] - np.asarray(t)),
+    "boundary_distance_signed": ("boundary_distance",
+                                 lambda F, idx, t: np.minimum(np.asarray(t) - F[idx], F[idx + 1] - np.asarray(t))),
 }
 
 
@@ -85,6 +90,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         lambda: E.test_decode_against_sdpa_per_head_and_gqa_mapping(),
         R.test_uniforms_follow_counter_layout,
         L.test_multinomial_indices_come_in_ascending_target_order,
+        E.test_boundary_distance_on_hand_built_cdf,
     ]
     assert _any_fails(pins), f"no pin caught the planted mistake {name!r}"
 
