@@ -41,13 +41,34 @@
  *
  * State: the library keeps none between calls on the host.  A workspace must
  * be all zero before its first call (santa_workspace_init, or any zero fill).
- * Every completed call leaves it all zero again (except for the error word at
- * byte 0 after a failed wait), so one workspace
- * large enough for each of them serves calls of any shapes, modes and sample
- * counts in any order.  The two-kernel path counts as one call from the start
- * of santa_score_pass to the end of the santa_sample_pass that follows it.
- * Calls that share a workspace must not overlap (same stream, or ordered by
- * events).
+ * Every completed call leaves it all zero again (except for the error word
+ * after a failed wait), the score stash and the multinomial targets included,
+ * so one workspace large enough for each of them serves calls of any shapes,
+ * modes and sample counts in any order (one problem's stash can lie where
+ * another's counts and records are).  The two-kernel path
+ * counts as one call from the start of santa_score_pass to the end of the
+ * santa_sample_pass that follows it.  Calls that share a workspace must not
+ * overlap (same stream, or ordered by events).
+ *
+ * Failed waits: the kernels that wait for other workgroups bound every wait
+ * (about two seconds).  A wait that gives up sets the workspace's error word
+ * (byte 0), and the workgroups that gave up write NaN to o and -1 to idx for
+ * their (sequence, KV head) group; the call still returns SANTA_STATUS_OK,
+ * because the failure happens after it returned.  Every later call on that
+ * workspace finds the word set and writes NaN / -1 for every group instead of
+ * computing, until santa_workspace_init clears it.  santa_workspace_status
+ * reads the word; it is the authoritative signal that a call's outputs are
+ * invalid (a group whose own splits did not wait may still hold finite values).
+ *
+ * Device residency: santa_decode's fused path (santa_decode_path() == 1) has
+ * the workgroups of one (sequence, KV head) wait for each other, which is
+ * safe only while the device holds every workgroup of the launch at once.
+ * The library checks that from the occupancy of an otherwise idle device.  A
+ * kernel running on the same device at the same time (another stream, another
+ * process) can keep workgroups from being placed until the waits give up.
+ * Callers that share the device with concurrent kernels pass
+ * SANTA_FLAG_TWO_KERNEL to santa_decode_args; the two-kernel path and
+ * santa_decode_flash never wait for a workgroup that has not started.
  */
 #ifndef SANTA_H
 #define SANTA_H
@@ -59,7 +80,7 @@
 extern "C" {
 #endif
 
-#define SANTA_ABI_VERSION 2
+#define SANTA_ABI_VERSION 3
 
 typedef enum santa_status {
     SANTA_STATUS_OK = 0,
@@ -263,6 +284,55 @@ santa_status santa_sample_pass(const santa_shape* shape, const void* q, const vo
                                const int32_t* block_table, int32_t num_samples, int32_t mode,
                                uint64_t seed, float* o, int32_t* idx, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Algorithms of santa_args. */
+enum {
+    SANTA_ALGO_PROP = 0,    /* santa_decode: exact global budget (section 3.2, S2ANTA-prop) */
+    SANTA_ALGO_FLASH = 1    /* santa_decode_flash: uniform tile budgets (section 3.3) */
+};
+
+/* Flags of santa_args. */
+enum {
+    SANTA_FLAG_TWO_KERNEL = 1u   /* SANTA_ALGO_PROP: never the fused kernel (see Device residency) */
+};
+
+/*
+ * Every argument of one decode step in one struct; the fields mean exactly
+ * what the arguments of the same names of santa_decode mean.
+ */
+typedef struct santa_args {
+    santa_shape shape;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* seq_lens;
+    const int32_t* block_table;
+    int32_t num_samples;
+    int32_t mode;
+    uint64_t seed;
+    float* o;
+    int32_t* idx;
+    void* workspace;
+    size_t workspace_bytes;
+    int32_t algorithm;      /* SANTA_ALGO_* */
+    uint32_t flags;         /* SANTA_FLAG_* (0: santa_decode's own path choice) */
+} santa_args;
+
+/*
+ * One decode step from a santa_args: santa_decode (SANTA_ALGO_PROP, honouring
+ * SANTA_FLAG_TWO_KERNEL) or santa_decode_flash (SANTA_ALGO_FLASH), with their
+ * statuses.  Unknown algorithms or flags give SANTA_STATUS_INVALID_ARGUMENT.
+ */
+santa_status santa_decode_args(const santa_args* args, void* stream);
+
+/*
+ * Reads the workspace's error word (nonzero: a bounded wait of a call that
+ * used this workspace gave up, see Failed waits) into *error_word.  It waits
+ * for the work already enqueued on `stream` (a host synchronisation, unlike
+ * every other call of this library).
+ */
+santa_status santa_workspace_status(const void* workspace, size_t workspace_bytes, void* stream,
+                                    uint32_t* error_word);
 
 #ifdef __cplusplus
 }

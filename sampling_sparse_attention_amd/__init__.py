@@ -19,7 +19,8 @@ __all__ = [
     "SantaError", "library", "library_path", "make_shape", "santa_workspace_layout_query",
     "santa_workspace_size", "santa_workspace_init", "santa_decode_path", "santa_decode",
     "santa_score_pass", "santa_sample_pass", "santa_decode_flash", "decode", "allocate_workspace",
-    "workspace_error",
+    "workspace_error", "validate", "Args", "santa_decode_args", "santa_workspace_status",
+    "ALGO_PROP", "ALGO_FLASH", "FLAG_TWO_KERNEL",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -28,12 +29,17 @@ MODE_STRATIFIED = 1
 MODE_SYSTEMATIC = 2
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
+_DTYPE_CODE = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}
 
 EXPORTED_SYMBOLS = (
     "santa_abi_version", "santa_status_string", "santa_last_error",
     "santa_workspace_layout_query", "santa_workspace_size", "santa_workspace_init",
     "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash",
+    "santa_decode_args", "santa_workspace_status",
 )
+ALGO_PROP = 0
+ALGO_FLASH = 1
+FLAG_TWO_KERNEL = 1
 PATH_FUSED = 1
 PATH_TWO_KERNELS = 2
 
@@ -63,6 +69,17 @@ class WorkspaceLayout(ctypes.Structure):
         ("records_offset", ctypes.c_size_t), ("stash_offset", ctypes.c_size_t),
         ("stash_row_bytes", ctypes.c_size_t), ("targets_offset", ctypes.c_size_t),
         ("split_size", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+    ]
+
+
+class Args(ctypes.Structure):
+    """Mirror of ``santa_args``."""
+    _fields_ = [
+        ("shape", Shape), ("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("num_samples", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("seed", ctypes.c_uint64), ("o", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("algorithm", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -97,6 +114,10 @@ def library() -> ctypes.CDLL:
         lib.santa_workspace_init.argtypes = [vp, sz, vp]
         lib.santa_decode_path.restype = i32
         lib.santa_decode_path.argtypes = [ctypes.POINTER(Shape), i32, i32]
+        lib.santa_decode_args.restype = ctypes.c_int
+        lib.santa_decode_args.argtypes = [ctypes.POINTER(Args), vp]
+        lib.santa_workspace_status.restype = ctypes.c_int
+        lib.santa_workspace_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
         for name in ("santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
@@ -127,7 +148,7 @@ def make_shape(q: torch.Tensor, k_cache: torch.Tensor, block_table: Optional[tor
         n_max = pages_per_seq * page_size
     if max_seq_len is not None:
         n_max = max_seq_len
-    dtype = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(q.dtype, -1)
+    dtype = _DTYPE_CODE.get(q.dtype, -1)
     st = k_cache.stride()
     return Shape(B, Hq, Hkv, d, n_max, page_size, pages_per_seq, num_pages, dtype, split_size,
                  st[0], st[1], st[2])
@@ -185,8 +206,70 @@ def _stream_handle(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def validate(shape: Shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, o, idx, workspace) -> None:
+    """Checks that the tensors match ``shape`` and the layouts of ``include/santa.h``
+    before anything reaches the library (the kernels trust the pointers they get:
+    a cache of another dtype or stride would be read out of bounds).  Raises
+    ``ValueError``."""
+    def need(cond, msg):
+        if not cond:
+            raise ValueError(msg)
+
+    tensors = {"q": q, "k_cache": k_cache, "v_cache": v_cache, "seq_lens": seq_lens, "o": o, "idx": idx,
+               "workspace": workspace}
+    if block_table is not None:
+        tensors["block_table"] = block_table
+    for name, t in tensors.items():
+        need(isinstance(t, torch.Tensor), f"{name} must be a torch.Tensor")
+    devices = {t.device for t in tensors.values()}
+    need(len(devices) == 1, f"all tensors must be on one device (got {sorted(map(str, devices))})")
+    need(q.dim() == 3 and q.is_contiguous(), "q must be a contiguous [B, Hq, d] tensor")
+    B, Hq, d = q.shape
+    need(q.dtype in _DTYPE_CODE, f"q must be bfloat16 or float32 (got {q.dtype})")
+    need(shape.dtype == _DTYPE_CODE[q.dtype], "shape.dtype does not match q.dtype")
+    need((shape.batch, shape.num_q_heads, shape.head_dim) == (B, Hq, d),
+         f"shape (batch {shape.batch}, heads {shape.num_q_heads}, head_dim {shape.head_dim}) "
+         f"does not match q {tuple(q.shape)}")
+    need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype,
+         f"k_cache and v_cache must have q's dtype {q.dtype} (got {k_cache.dtype}, {v_cache.dtype})")
+    need(k_cache.dim() == 4, "k_cache must be 4-D ([B, n_max, Hkv, d] or [pages, page_size, Hkv, d])")
+    need(v_cache.shape == k_cache.shape, f"v_cache shape {tuple(v_cache.shape)} differs from k_cache "
+                                         f"{tuple(k_cache.shape)}")
+    need(v_cache.stride() == k_cache.stride(), f"v_cache strides {v_cache.stride()} differ from k_cache "
+                                               f"{k_cache.stride()}")
+    need(k_cache.stride(-1) == 1, "the head dimension of the caches must be contiguous (stride 1)")
+    need(k_cache.shape[2] == shape.num_kv_heads and k_cache.shape[3] == d,
+         f"cache KV heads / head_dim {tuple(k_cache.shape[2:])} do not match the shape "
+         f"({shape.num_kv_heads}, {d})")
+    need(tuple(k_cache.stride()[:3]) == (shape.kv_stride_seq, shape.kv_stride_tok, shape.kv_stride_head),
+         "shape's KV strides do not match k_cache.stride()")
+    if shape.page_size == 0:
+        need(block_table is None, "block_table given for a contiguous cache (shape.page_size == 0)")
+        need(k_cache.shape[0] >= B and k_cache.shape[1] >= shape.max_seq_len,
+             f"contiguous cache {tuple(k_cache.shape[:2])} smaller than (batch {B}, max_seq_len "
+             f"{shape.max_seq_len})")
+    else:
+        need(block_table is not None, "a paged cache (shape.page_size > 0) needs block_table")
+        need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+             "block_table must be a contiguous int32 [B, pages_per_seq] tensor")
+        need(tuple(block_table.shape) == (B, shape.pages_per_seq),
+             f"block_table shape {tuple(block_table.shape)} is not (batch {B}, pages_per_seq "
+             f"{shape.pages_per_seq})")
+        need(k_cache.shape[0] == shape.num_pages and k_cache.shape[1] == shape.page_size,
+             f"paged cache {tuple(k_cache.shape[:2])} is not (num_pages {shape.num_pages}, page_size "
+             f"{shape.page_size})")
+    need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,) and seq_lens.is_contiguous(),
+         "seq_lens must be a contiguous int32 [B] tensor")
+    need(o.dtype == torch.float32 and tuple(o.shape) == (B, Hq, d) and o.is_contiguous(),
+         "o must be a contiguous float32 [B, Hq, d] tensor")
+    need(idx.dtype == torch.int32 and tuple(idx.shape) == (B, Hq, num_samples) and idx.is_contiguous(),
+         f"idx must be a contiguous int32 [B, Hq, {num_samples}] tensor")
+    need(workspace.is_contiguous(), "workspace must be contiguous")
+
+
 def _call(name, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o, idx,
           workspace, stream):
+    validate(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, o, idx, workspace)
     fn = getattr(library(), name)
     _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
               _ptr(block_table), int(num_samples), int(mode), ctypes.c_uint64(seed & (2 ** 64 - 1)),
@@ -206,6 +289,26 @@ def santa_decode_flash(shape, q, k_cache, v_cache, seq_lens, block_table, num_sa
     """One S^2ANTA-flash decode step (``santa_decode_flash`` of the C ABI)."""
     _call("santa_decode_flash", shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode,
           seed, o, idx, workspace, stream)
+
+
+def santa_decode_args(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o, idx,
+                      workspace, algorithm=ALGO_PROP, flags=0, stream=None) -> None:
+    """One decode step through the struct entry point (``santa_decode_args`` of the C ABI)."""
+    validate(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, o, idx, workspace)
+    a = Args(shape, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+             None if block_table is None else block_table.data_ptr(), int(num_samples), int(mode),
+             seed & (2 ** 64 - 1), o.data_ptr(), idx.data_ptr(), workspace.data_ptr(),
+             workspace.numel() * workspace.element_size(), int(algorithm), int(flags))
+    _check(library().santa_decode_args(ctypes.byref(a), _stream_handle(stream)), "santa_decode_args")
+
+
+def santa_workspace_status(workspace: torch.Tensor, stream=None) -> int:
+    """The workspace's error word through the C ABI (``santa_workspace_status``); waits
+    for the stream's enqueued work."""
+    out = ctypes.c_uint32()
+    _check(library().santa_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream), ctypes.byref(out)), "santa_workspace_status")
+    return out.value
 
 
 def santa_score_pass(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o,

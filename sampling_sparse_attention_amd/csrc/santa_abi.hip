@@ -227,7 +227,8 @@ enum Stage { kScore = 1, kSample = 2, kDecode = 3 };
 
 santa_status run(int stages, const santa_shape* s, const void* q, const void* k, const void* v,
                  const int32_t* seq_lens, const int32_t* block_table, int32_t S, int32_t mode,
-                 uint64_t seed, float* o, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+                 uint64_t seed, float* o, int32_t* idx, void* ws, size_t ws_bytes, void* stream,
+                 uint32_t flags = 0) {
     santa::Params p;
     Plan plan;
     santa_status st = make_params(s, q, k, v, seq_lens, block_table, S, mode, seed, o, idx, ws,
@@ -235,7 +236,7 @@ santa_status run(int stages, const santa_shape* s, const void* q, const void* k,
     if (st != SANTA_STATUS_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int path = 2;
-    if (stages == kDecode) {
+    if (stages == kDecode && !(flags & SANTA_FLAG_TWO_KERNEL)) {
         path = choose_path(p, s->dtype);
         if (path == 0) return fail(SANTA_STATUS_HIP_ERROR, "querying the device for the launch plan failed");
     }
@@ -364,6 +365,42 @@ santa_status santa_decode_flash(const santa_shape* shape, const void* q, const v
     st = hip_check(santa::launch_flash(p, shape->dtype, static_cast<hipStream_t>(stream)),
                    "launching the flash decode kernel");
     if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_decode_args(const santa_args* a, void* stream) {
+    if (!a) return fail(SANTA_STATUS_INVALID_ARGUMENT, "args is NULL");
+    if (a->flags & ~(uint32_t)SANTA_FLAG_TWO_KERNEL)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "unknown flags 0x%x", a->flags);
+    switch (a->algorithm) {
+        case SANTA_ALGO_PROP:
+            return run(kDecode, &a->shape, a->q, a->k_cache, a->v_cache, a->seq_lens, a->block_table,
+                       a->num_samples, a->mode, a->seed, a->o, a->idx, a->workspace, a->workspace_bytes, stream,
+                       a->flags);
+        case SANTA_ALGO_FLASH:
+            return santa_decode_flash(&a->shape, a->q, a->k_cache, a->v_cache, a->seq_lens, a->block_table,
+                                      a->num_samples, a->mode, a->seed, a->o, a->idx, a->workspace,
+                                      a->workspace_bytes, stream);
+    }
+    return fail(SANTA_STATUS_INVALID_ARGUMENT, "unknown algorithm %d", a->algorithm);
+}
+
+santa_status santa_workspace_status(const void* workspace, size_t workspace_bytes, void* stream,
+                                    uint32_t* error_word) {
+    if (!workspace || !error_word) return fail(SANTA_STATUS_INVALID_ARGUMENT, "workspace or error_word is NULL");
+    if (!aligned(workspace, 256)) return fail(SANTA_STATUS_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    if (workspace_bytes < santa::kSyncBytes)
+        return fail(SANTA_STATUS_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs at least %zu",
+                    workspace_bytes, santa::kSyncBytes);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    santa_status st = hip_check(hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, hs),
+                                "reading the workspace's error word");
+    if (st != SANTA_STATUS_OK) return st;
+    st = hip_check(hipStreamSynchronize(hs), "waiting for the stream");
+    if (st != SANTA_STATUS_OK) return st;
+    *error_word = word;
     g_error[0] = '\0';
     return SANTA_STATUS_OK;
 }

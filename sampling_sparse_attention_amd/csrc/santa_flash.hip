@@ -25,6 +25,7 @@ void flash_kernel(Params p) {
     const Item at = item_coords(p, blockIdx.x);
     uint4 qf[G];
     load_q<G, D, E, NT>(p, at.b, at.g, qf);
+    const unsigned int err0 = p.sync->error;    // nonzero: an earlier call left stale state
     const Item it = make_item(p, blockIdx.x);
     if (it.n == 0) {
         if (it.t == 0) write_empty<G, D, NT>(p, it);
@@ -40,7 +41,13 @@ void flash_kernel(Params p) {
     load_pages<NT>(p, it, pages);
     __syncthreads();
     stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
+    __shared__ unsigned int s_err;      // thread 0's read, the same for the whole workgroup
+    if (threadIdx.x == 0) s_err = err0;
     __syncthreads();
+    if (s_err) {                // the reference maxima, slots and counts are not to be trusted
+        if (it.t == 0) poison_group<G, D, NT>(p, it);
+        return;
+    }
     split_stats<G, NT, false>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     __syncthreads();            // the scores' LDS is reused for the sampling below
 

@@ -14,7 +14,7 @@ namespace santa {
 
 template <int G, int D, typename E, int NT>
 __device__ __forceinline__ void fused_item(const Params& p, const Item& it, const uint4 (&qf)[G],
-                                           unsigned char* smem) {
+                                           unsigned int err0, unsigned char* smem) {
     if (it.n == 0) {
         if (it.t == 0) write_empty<G, D, NT>(p, it);
         return;
@@ -25,17 +25,30 @@ __device__ __forceinline__ void fused_item(const Params& p, const Item& it, cons
     int* pages = reinterpret_cast<int*>(smem + L.pages);
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
 
+    __shared__ int s_fail;              // a wait of this workgroup gave up
+    if (threadIdx.x == 0) s_fail = 0;
     load_pages<NT>(p, it, pages);
     __syncthreads();
     stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
+    __shared__ unsigned int s_err;      // thread 0's read, the same for the whole workgroup
+    if (threadIdx.x == 0) s_err = err0;
     __syncthreads();
+    // an earlier call left the workspace in error: its counts and records are
+    // stale, so nothing of this call can be trusted
+    if (s_err) {
+        if (it.t == 0) poison_group<G, D, NT>(p, it);
+        return;
+    }
     // each head's wave publishes its record; a reader re-reads a record until it
     // is written, so neither a workgroup barrier nor the stores' completion is
     // needed before the count at the group barrier
     split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
-    group_barrier(p, it, [&] { systematic_offsets<G, 1>(p, it, hs); });
-    prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit);
-    finish_output<G, D, NT>(p, it);
+    if (!group_barrier(p, it, [&] { systematic_offsets<G, 1>(p, it, hs); })) {
+        poison_group<G, D, NT>(p, it);      // the barrier's result is the same in every thread
+        return;
+    }
+    prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit, &s_fail);
+    finish_output<G, D, NT>(p, it, &s_fail);
 }
 
 // Four waves per SIMD (all 1024 splits of a batch-1, 8-KV-head, 32k-token
@@ -48,7 +61,8 @@ void fused_kernel(Params p) {
     uint4 qf[G];
     priority_streaming();
     load_q<G, D, E, NT>(p, at.b, at.g, qf);
-    fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), qf, smem);
+    const unsigned int err0 = p.sync->error;    // in flight with q, used after the K stream
+    fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), qf, err0, smem);
 }
 
 template <int G, int D, typename E>

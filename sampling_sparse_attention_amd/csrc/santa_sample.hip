@@ -15,6 +15,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 :
 void sample_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Item it = make_item(p, blockIdx.x);
+    const unsigned int err0 = p.sync->error;    // nonzero: an earlier call left stale state
     if (it.n == 0) {
         if (it.t == 0) write_empty<G, D, NT>(p, it);
         return;
@@ -24,9 +25,17 @@ void sample_kernel(Params p) {
     float* sc = reinterpret_cast<float*>(smem + L.scratch);
     int* pages = reinterpret_cast<int*>(smem + L.pages);
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
+    __shared__ int s_fail;              // a head found records missing
+    __shared__ unsigned int s_err;      // thread 0's read of the error word
+    if (threadIdx.x == 0) {
+        s_fail = 0;
+        s_err = err0;
+    }
     load_pages<NT>(p, it, pages);
     // the split's stash slice, which no other workgroup reads, is returned to
-    // zero as it is read
+    // zero as it is read: the workspace may next serve a problem of another
+    // layout, whose records, counts and slots can lie in these bytes and must
+    // read zero
     for (int i = threadIdx.x; i < G * p.split; i += NT) {
         const int h = i / p.split;
         const int k = i - h * p.split;
@@ -40,10 +49,14 @@ void sample_kernel(Params p) {
     split_stats<G, NT, false>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     systematic_offsets<G, 0>(p, it, hs);
     __syncthreads();
+    if (s_err) {                        // an earlier call left stale state
+        if (it.t == 0) poison_group<G, D, NT>(p, it);
+        return;
+    }
     // the records come from the score pass, an earlier launch: one missing now
     // means no score pass preceded this one, which is an error, not a wait
-    prefix_and_sample<G, D, E, NT>(p, it, L, smem, 0);
-    finish_output<G, D, NT>(p, it);
+    prefix_and_sample<G, D, E, NT>(p, it, L, smem, 0, &s_fail);
+    finish_output<G, D, NT>(p, it, &s_fail);
 }
 
 template <int G, int D, typename E>

@@ -951,12 +951,14 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
 // Split masses w_j = l_j * exp(m_j - M) are summed as fixed point with 2^-40
 // resolution, so the prefix W is exact, monotone and identical in every
 // workgroup of the sequence, and the ranges [W_t, W_t+1) tile [0, Z).
-// Records still missing after `spin_limit` re-reads set the error word.
-// Returns false if the wait gave up.
+// Records still missing after `spin_limit` re-reads set the error word and
+// *fail (shared by the workgroup, read by finish_output after its barrier),
+// and the head is skipped: nothing is computed from an incomplete set of
+// records.
 // ---------------------------------------------------------------------------
 template <int G, int D, typename E, int NT>
-__device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
-                                                  unsigned char* smem, int spin_limit) {
+__device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
+                                                  unsigned char* smem, int spin_limit, int* fail) {
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
@@ -965,7 +967,6 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
     // records per lane: the power of two K = 2^ks with 64 K >= Tb (K <= kRecPerLane)
     const int ks = Tb <= 64 ? 0 : Tb <= 128 ? 1 : Tb <= 256 ? 2 : 3;
     const int K = 1 << ks;
-    bool ok_all = true;
     for (int h = wave; h < G; h += NW) {
         const int hq = it.g * G + h;
         const unsigned long long* rec = record_of(p, it.b, hq, 0);
@@ -987,6 +988,7 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
                 lr[k] = __uint_as_float((uint32_t)(r >> 32));
             }
         }
+        bool gave_up = false;
         for (int iter = 0; !__all(fresh); ++iter) {
             bool ok = true;
 #pragma unroll
@@ -1004,13 +1006,16 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
             }
             if (__all(ok)) break;
             if (iter >= spin_limit) {
-                ok_all = false;
-                if (lane == 0)
+                gave_up = true;
+                if (lane == 0) {
                     __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    *fail = 1;
+                }
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
         }
+        if (gave_up) continue;      // the same in every lane of the wave
         float mx = -INFINITY;
 #pragma unroll
         for (int k = 0; k < kRecPerLane; ++k) mx = fmaxf(mx, mr[k]);
@@ -1072,7 +1077,28 @@ __device__ __forceinline__ bool prefix_and_sample(const Params& p, const Item& i
             });
         }
     }
-    return ok_all;
+}
+
+// ---------------------------------------------------------------------------
+// Failed calls.  A bounded wait that gives up sets the workspace's error word;
+// the splits that gave up write NaN to o and -1 to idx for their group's heads
+// and stop, so the group's counts are left unfinished (the workspace needs
+// santa_workspace_init).  A later call that finds the error word set at its
+// start does the same for every group instead of consuming the stale state,
+// and the split that would finish a group's output writes NaN if the error
+// word is set by then.  The error word itself is the authoritative signal:
+// a split of a group that did not wait may still have finished it first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned int workspace_error_now(const Params& p) {
+    return __hip_atomic_load(&p.sync->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int G, int D, int NT>
+__device__ __forceinline__ void poison_group(const Params& p, const Item& it) {
+    float* o = p.o + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D;
+    for (int i = threadIdx.x; i < G * D; i += NT) o[i] = __builtin_nanf("");
+    int32_t* idx = p.idx + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
+    for (int i = threadIdx.x; i < G * p.S; i += NT) idx[i] = -1;
 }
 
 // Waits until every memory operation this wave has issued has completed.
@@ -1086,13 +1112,19 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // slots, stores o = (1/S) * sum (Eq. 3) for the G heads, and returns to zero
 // the slots, the counts, the barrier flags, the group's split records and
 // (multinomial) its targets, so that a completed call leaves this state all
-// zero.  Nothing here waits for another workgroup.
+// zero: the next call may have another layout, whose synchronisation state
+// can lie where this call's targets were.  Nothing here waits for another
+// workgroup.
 // ---------------------------------------------------------------------------
 template <int G, int D, int NT>
-__device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
+__device__ __forceinline__ void finish_output(const Params& p, const Item& it, const int* fail) {
     __shared__ int s_last;
     wait_memory();           // this wave's slot additions have been performed
     __syncthreads();
+    if (*fail) {             // a head's wait gave up: the group is not finished
+        poison_group<G, D, NT>(p, it);
+        return;
+    }
     unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
     if (threadIdx.x == 0) {
         const unsigned int prev = __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1105,7 +1137,8 @@ __device__ __forceinline__ void finish_output(const Params& p, const Item& it) {
     unsigned long long* acc =
         reinterpret_cast<unsigned long long*>(p.accum + ((int64_t)it.b * p.Hkv + it.g) * kOutSlots * G * D);
     float* o = p.o + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * D;
-    const float inv_s = 1.0f / (float)p.S;
+    // a wait of this call gave up somewhere: the output is not trusted
+    const float inv_s = workspace_error_now(p) ? __builtin_nanf("") : 1.0f / (float)p.S;
     for (int i = threadIdx.x; i < NP; i += NT) {
         unsigned long long v[kOutSlots];
 #pragma unroll

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert len(declared) == 11
+    assert len(declared) == 13
     out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (santa_\w+)", out))
@@ -196,3 +196,62 @@ def test_flash_rejects_multinomial_and_too_few_samples_before_launch(lib):
     lay = santa.santa_workspace_layout_query(shape, 64, 2)
     assert lay.accum_offset < lay.flash_offset < lay.records_offset
     assert lay.records_offset - lay.flash_offset >= 256 + 32 * 16 * 130 * 8   # refs, then fp64 slots
+
+
+def test_args_struct_matches_header_layout(lib):
+    """The ctypes mirror of santa_args has the C layout (fields in header order, natural
+    alignment), checked against offsets computed by the host compiler from santa.h."""
+    import tempfile
+    src = r'''
+#include <stddef.h>
+#include <stdio.h>
+#include "santa.h"
+#define F(x) printf("%s %zu\n", #x, offsetof(santa_args, x));
+int main(void) {
+    F(shape) F(q) F(k_cache) F(v_cache) F(seq_lens) F(block_table) F(num_samples) F(mode) F(seed)
+    F(o) F(idx) F(workspace) F(workspace_bytes) F(algorithm) F(flags)
+    printf("size %zu\n", sizeof(santa_args));
+    return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "off.c")
+        exe = os.path.join(d, "off")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    want = dict(line.split() for line in out.strip().splitlines())
+    for name, _ in santa.Args._fields_:
+        assert getattr(santa.Args, name).offset == int(want[name]), name
+    assert ctypes.sizeof(santa.Args) == int(want["size"])
+
+
+def test_decode_args_validates_before_launch(lib):
+    shape = _shape(max_seq_len=1024, kv_stride_seq=1024 * 8 * 128)
+    need = santa.santa_workspace_size(shape, 64, 2)
+    fake = 1 << 20
+
+    def call(**kw):
+        a = santa.Args(shape, fake, fake, fake, fake, None, 64, 2, 0, fake, fake, fake, need, 0, 0)
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return lib.santa_decode_args(ctypes.byref(a), None)
+
+    assert lib.santa_decode_args(None, None) == INVALID
+    assert call(algorithm=2) == INVALID
+    assert "algorithm" in lib.santa_last_error().decode()
+    assert call(flags=2) == INVALID
+    assert call(q=None) == INVALID
+    assert call(workspace_bytes=need - 1) == WS_SMALL
+    need0 = santa.santa_workspace_size(shape, 64, 0)
+    assert call(algorithm=1, mode=0, workspace_bytes=need0) == UNSUPPORTED   # flash: stratified/systematic
+    assert call(flags=1, num_samples=0) == INVALID
+
+
+def test_workspace_status_validates_before_touching_the_device(lib):
+    word = ctypes.c_uint32(7)
+    assert lib.santa_workspace_status(None, 4096, None, ctypes.byref(word)) == INVALID
+    assert lib.santa_workspace_status(ctypes.c_void_p(1 << 20), 4096, None, None) == INVALID
+    assert lib.santa_workspace_status(ctypes.c_void_p((1 << 20) + 4), 4096, None, ctypes.byref(word)) == INVALID
+    assert lib.santa_workspace_status(ctypes.c_void_p(1 << 20), 16, None, ctypes.byref(word)) == WS_SMALL
+    assert word.value == 7

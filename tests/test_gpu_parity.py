@@ -278,7 +278,11 @@ def test_sample_pass_without_score_pass_sets_error():
     santa.santa_sample_pass(*args)                 # fresh workspace: no records
     torch.cuda.synchronize()
     assert santa.workspace_error(ws) != 0
+    assert santa.santa_workspace_status(ws) != 0
+    # every group gave up: NaN outputs and idx = -1 (sequences with keys)
+    assert torch.isnan(o).all() and bool((idx == -1).all())
     santa.santa_workspace_init(ws)
+    assert santa.santa_workspace_status(ws) == 0
     santa.santa_score_pass(*args)
     santa.santa_sample_pass(*args)
     torch.cuda.synchronize()
@@ -357,3 +361,69 @@ def test_toy_unbiased_over_4096_seeds():
             ref = H.oracle_head(x, 0, 0, 64, mode, seed)
             H.check_head(H.ParityReport(), ref, idx[0, 0].cpu().numpy().astype(np.int64),
                          o[0, 0].double().cpu().numpy(), f"toy seed {seed}")
+
+
+@pytest.mark.parametrize("path", ["fused", "two_kernel", "flash"])
+def test_call_on_a_workspace_in_error_poisons_every_group(path):
+    """A workspace whose error word is set (here by the host) holds stale state: a call on it
+    writes NaN to o and -1 to idx for every group instead of computing, leaves the word set,
+    and santa_workspace_init makes the workspace usable again."""
+    x = _inputs(lens=(1000, 1537, 64))
+    S, mode = 64, 2
+    shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len)
+    B, Hq, d = x["q"].shape
+    o = torch.zeros((B, Hq, d), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((B, Hq, S), dtype=torch.int32, device="cuda")
+    ws = santa.allocate_workspace(shape, S, mode, "cuda")
+    ws[0:4].view(torch.int32).fill_(1)
+    algo = santa.ALGO_FLASH if path == "flash" else santa.ALGO_PROP
+    flags = santa.FLAG_TWO_KERNEL if path == "two_kernel" else 0
+    args = (shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, 9, o, idx, ws)
+    if path == "two_kernel":
+        santa.santa_score_pass(*args)
+        santa.santa_sample_pass(*args)
+    else:
+        santa.santa_decode_args(*args, algorithm=algo, flags=flags)
+    assert santa.santa_workspace_status(ws) == 1
+    assert torch.isnan(o).all() and bool((idx == -1).all())
+    santa.santa_workspace_init(ws)
+    santa.santa_decode_args(*args, algorithm=algo, flags=flags)
+    assert santa.santa_workspace_status(ws) == 0
+    if path == "flash":
+        tile = santa.santa_workspace_layout_query(shape, S, mode).split_size
+        H.check_flash(x, S, mode, 9, tile, o.cpu(), idx.cpu())
+    else:
+        H.check_all(x, S, mode, 9, o.cpu(), idx.cpu())
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_args_entry_point_and_forced_two_kernel_path(mode):
+    """santa_decode_args gives santa_decode's indices on either path (the fused kernel by
+    default on this shape, the score and sample passes with SANTA_FLAG_TWO_KERNEL), and
+    santa_decode_flash's with SANTA_ALGO_FLASH."""
+    x = _inputs(lens=(2000, 1537, 64, 1))
+    S = 96
+    shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len)
+    assert santa.santa_decode_path(shape, S, mode) == santa.PATH_FUSED
+    B, Hq, d = x["q"].shape
+    ws = santa.allocate_workspace(shape, S, mode, "cuda")
+    outs = []
+    for flags in (0, santa.FLAG_TWO_KERNEL):
+        o = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+        idx = torch.full((B, Hq, S), -7, dtype=torch.int32, device="cuda")
+        santa.santa_decode_args(shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, 21, o, idx, ws,
+                                flags=flags)
+        torch.cuda.synchronize()
+        H.check_all(x, S, mode, 21, o.cpu(), idx.cpu())
+        outs.append(idx.cpu())
+    assert torch.equal(outs[0], outs[1])
+    assert santa.santa_workspace_status(ws) == 0
+    if mode != 0:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        i1 = torch.empty((B, Hq, S), dtype=torch.int32, device="cuda")
+        i2 = torch.empty_like(i1)
+        santa.santa_decode_args(shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, 21, o, i1, ws,
+                                algorithm=santa.ALGO_FLASH)
+        santa.santa_decode_flash(shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, 21, o, i2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(i1.cpu(), i2.cpu())
