@@ -2,27 +2,31 @@
 
 A step is one ``santa_decode`` call over one batch of synthetic input: the
 fused kernel (scores, global partition function, sampling and gather in one
-launch), plus the target sort for multinomial sampling.  The default workload is the Llama-3.1-8B-shaped layer:
-batch 1, 32 query / 8 KV heads, d = 128, 32768 bf16 keys, S = 256 systematic
-samples.  ``--kv-copies`` independent caches (default 8, 1 GiB) are cycled
-through, one per step like the layers of a model, so that K is read from HBM
-and not from the 256 MB Infinity Cache.
+launch), plus the target sort for multinomial sampling.  The default workload is
+the Llama-3.1-8B-shaped layer: batch 1, 32 query / 8 KV heads, d = 128, 32768
+bf16 keys, S = 256 systematic samples.  ``--kv-copies`` independent caches
+(default 8, 1 GiB) are cycled through, one per step like the layers of a model,
+so that K is read from HBM and not from the 256 MB Infinity Cache.
 
-The timed steps are graph replays split into 10 rounds; the line reports the mean
-over all of them as the value and, beside it, the median of the round means with
-a 95 % bootstrap interval.
+Timing: exactly ``--steps`` calls are timed with HIP events on the launch stream,
+replayed from HIP graphs of a few calls each, in ``min(20, steps)`` rounds of
+equal length; ``value`` comes from the whole timed interval, and the line also
+gives the median of the per-round times with a 95 % bootstrap interval.
 
-Prints one JSON line: throughput in heads x batch per second, the roofline of
-the dominant kernel (the fused decode kernel, bound by HBM bandwidth: all of K
-plus the distinct sampled V rows per launch), the two-kernel path's stage
-times for comparison, and the CPU oracle timed on a bounded sample of the same
-workload.
+The JSON line also carries: the roofline of the dominant kernel (the fused
+decode kernel, bound by HBM bandwidth: all of K plus the distinct sampled V rows
+per launch), the HBM bandwidth of a plain device copy measured in the same run,
+the two-kernel path and S^2ANTA-flash on the same inputs, the Qwen2.5-7B-shaped
+long-context step (all three sampling rules), a parity sample of the timed
+configuration against the oracle (boundary cases, largest CDF difference), and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -38,6 +42,9 @@ import workloads as W  # noqa: E402
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "decode attention steps/sec (heads×batch) at 32k ctx; achieved HBM GB/s vs peak"
 KERNEL_SOURCES = ["santa_fused.hip", "santa_split.h", "santa_device.h", "santa_internal.h"]
+ROUNDS = 20                    # timed rounds (fewer only if fewer calls are timed)
+MAX_GRAPH_CALLS = 32           # calls captured per HIP graph
+BOUNDARY_WINDOW = 1e-6
 
 
 def strip_comments(text: str) -> str:
@@ -76,10 +83,10 @@ def counter_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=4000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama32k", choices=sorted(W.WORKLOADS))
     ap.add_argument("--samples", type=int, default=None)
@@ -88,16 +95,17 @@ def parse():
     ap.add_argument("--kv-copies", type=int, default=8)
     ap.add_argument("--eager", action="store_true", help="launch every call from Python, no HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline step (no two-kernel, flash, Qwen or copy lines)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run plain device-to-device copies of BYTES bytes (the reference kernel "
                          "for scaling HBM byte counters) and print their bandwidth")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
-def calibrate_copy(nbytes: int, reps: int = 10):
-    """Plain copies of a known size: what FETCH_SIZE / WRITE_SIZE read for them
-    converts the counters of the SANTA kernels into bytes."""
+def copy_bandwidth(nbytes: int, reps: int = 10):
+    """Device-to-device copies of `nbytes`: seconds per copy and (read + write) GB/s."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -109,15 +117,13 @@ def calibrate_copy(nbytes: int, reps: int = 10):
     end.record()
     torch.cuda.synchronize()
     t = start.elapsed_time(end) / reps * 1e-3
-    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps, "copy_us": t * 1e6,
-                      "read_plus_write_gbs": 2 * nbytes / t / 1e9}))
+    del src, dst
+    torch.cuda.empty_cache()
+    return t, 2 * nbytes / t / 1e9
 
 
 def make_copies(w, n, device):
-    copies = []
-    for c in range(n):
-        copies.append(W.make_inputs(w, seed=c, device=device))
-    return copies
+    return [W.make_inputs(w, seed=c, device=device) for c in range(n)]
 
 
 class Runner:
@@ -137,72 +143,90 @@ class Runner:
         self.ws = santa.allocate_workspace(self.shape, S, mode, dev)
         self.seed = x["workload"].sample_seed
 
-    def _args(self, c):
+    def args(self, c):
         x = self.copies[c % len(self.copies)]
         return (self.shape, x["q"], x["k"], x["v"], x["seq_lens"], x["block_table"], self.S, self.mode,
                 self.seed, self.o, self.idx, self.ws)
 
     def step(self, c):
-        self.santa.santa_decode(*self._args(c))
+        self.santa.santa_decode(*self.args(c))
 
-    def score(self, c):
-        self.santa.santa_score_pass(*self._args(c))
+    def two_kernel(self, c):
+        self.santa.santa_score_pass(*self.args(c))
+        self.santa.santa_sample_pass(*self.args(c))
 
-    def sample(self, c):
-        self.santa.santa_sample_pass(*self._args(c))
+    def flash(self, c):
+        self.santa.santa_decode_flash(*self.args(c))
 
 
-def timed(fn, reps, eager, ncopies):
-    """Average GPU time per call of fn(c), measured with events on the launch
-    stream: replays of a captured graph of `ncopies` calls, or eager calls."""
+def graph_plan(steps: int, ncopies: int, rounds: int = ROUNDS):
+    """How `steps` timed calls are replayed: (calls per graph L, graphs P, replays,
+    rounds).  L is the largest divisor of `steps` that leaves at least `rounds`
+    replays (at most MAX_GRAPH_CALLS), so exactly `steps` calls run; graph j holds
+    calls j*L .. j*L + L - 1, whose KV copies continue where graph j - 1 stopped,
+    and the pattern repeats after P graphs."""
+    # at least 10 rounds when there are 10 calls, up to `rounds` while graphs stay full
+    nr = max(1, min(10, steps), min(rounds, steps // MAX_GRAPH_CALLS))
+    cap = max(1, min(MAX_GRAPH_CALLS, steps // nr))
+    L = max(d for d in range(1, cap + 1) if steps % d == 0)
+    P = ncopies // math.gcd(L, ncopies)
+    return L, P, steps // L, nr
+
+
+def timed(fn, steps, eager, ncopies):
+    """Times exactly `steps` calls fn(i) (call i on KV copy i mod ncopies) with events
+    on the launch stream.  Returns (seconds per call over the whole interval, seconds
+    per call of each round, calls timed)."""
     stream = torch.cuda.current_stream()
     if eager:
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nr = max(1, min(ROUNDS, steps))
+        marks = [round(r * steps / nr) for r in range(nr + 1)]
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(nr + 1)]
         torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(reps):
-            fn(i)
-        end.record(stream)
+        events[0].record(stream)
+        for r in range(nr):
+            for i in range(marks[r], marks[r + 1]):
+                fn(i)
+            events[r + 1].record(stream)
         torch.cuda.synchronize()
-        return start.elapsed_time(end) / reps * 1e-3
-    per_graph = ncopies * max(1, 32 // ncopies)
+        per_round = [events[r].elapsed_time(events[r + 1]) * 1e-3 / (marks[r + 1] - marks[r]) for r in range(nr)]
+        return events[0].elapsed_time(events[-1]) * 1e-3 / steps, per_round, steps
+    L, P, replays, nr = graph_plan(steps, ncopies)
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        for i in range(per_graph):
+        for i in range(P * L):
             fn(i)
     stream.wait_stream(side)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(per_graph):
-            fn(i)
+    graphs = []
+    for j in range(P):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(L):
+                fn(j * L + i)
+        graphs.append(g)
     torch.cuda.synchronize()
-    replays = max(1, reps // per_graph)
-    graph.replay()
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
-    # events at round boundaries (ROUNDS rounds of about equal length) on the
-    # launch stream; the whole interval gives the mean, the rounds its spread
-    nr = min(ROUNDS, replays)
-    marks = [round(i * replays / nr) for i in range(nr + 1)]
+    marks = [round(r * replays / nr) for r in range(nr + 1)]
     events = [torch.cuda.Event(enable_timing=True) for _ in range(nr + 1)]
     events[0].record(stream)
     for r in range(nr):
-        for _ in range(marks[r + 1] - marks[r]):
-            graph.replay()
+        for k in range(marks[r], marks[r + 1]):
+            graphs[k % P].replay()
         events[r + 1].record(stream)
     torch.cuda.synchronize()
-    LAST_ROUNDS[:] = [events[r].elapsed_time(events[r + 1]) / ((marks[r + 1] - marks[r]) * per_graph) * 1e-3
-                      for r in range(nr)]
-    return events[0].elapsed_time(events[-1]) / (replays * per_graph) * 1e-3
-
-
-ROUNDS = 10
-LAST_ROUNDS = []        # seconds per call in each round of the last graph-timed call of timed()
+    per_round = [events[r].elapsed_time(events[r + 1]) * 1e-3 / ((marks[r + 1] - marks[r]) * L) for r in range(nr)]
+    calls = replays * L
+    del graphs
+    return events[0].elapsed_time(events[-1]) * 1e-3 / calls, per_round, calls
 
 
 def round_stats(rounds, seed=0, n_boot=2000):
-    """Median of the per-round times and a 95 % bootstrap interval of it (seconds)."""
+    """Median of the per-round times and a 95 % bootstrap interval of it (seconds in,
+    microseconds out)."""
     import numpy as np
     x = np.asarray(rounds, dtype=np.float64)
     if x.size == 0:
@@ -214,43 +238,142 @@ def round_stats(rounds, seed=0, n_boot=2000):
             "min_us": float(x.min()) * 1e6, "max_us": float(x.max()) * 1e6}
 
 
-def cpu_baseline(w, x_gpu, S, mode, seconds):
-    """The oracle on the host: full decode steps of the same workload (all heads),
-    repeated until about `seconds` of CPU time."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_arrays(x):
+    q = x["q"].double().cpu().numpy()
+    k = x["k"].cpu().float().numpy()
+    v = x["v"].cpu().float().numpy()
+    lens = x["seq_lens"].cpu().numpy()
+    bt = None if x["block_table"] is None else x["block_table"].cpu().numpy()
+    return q, k, v, lens, bt
+
+
+def parity_sample(santa, run, w, S, mode, heads):
+    """The timed configuration (KV copy 0, the timed launch) against the oracle on
+    `heads`: idx exact outside the 1e-6 boundary window, boundary cases counted, o
+    against the oracle's fp64 gather of the GPU's own idx.  The largest CDF
+    difference compares the oracle's CDF with the one built (in fp64) from the
+    GPU's own fp32 scores, read from the score pass's stash; the sample pass that
+    follows consumes and clears the stash again."""
     import numpy as np
     from oracle import santa as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        blas = 1
-    q = x_gpu["q"].double().cpu().numpy()
-    k = x_gpu["k"].cpu().float().numpy()
-    v = x_gpu["v"].cpu().float().numpy()
-    lens = x_gpu["seq_lens"].cpu().numpy()
-    bt = None if x_gpu["block_table"] is None else x_gpu["block_table"].cpu().numpy()
+    run.step(0)
+    torch.cuda.synchronize()
+    idx_gpu = run.idx.cpu().numpy().astype(np.int64)
+    o_gpu = run.o.cpu().double().numpy()
+    lay = santa.santa_workspace_layout_query(run.shape, S, mode)
+    santa.santa_score_pass(*run.args(0))
+    torch.cuda.synchronize()
+    B, Hq = w.batch, w.q_heads
+    row = lay.stash_row_bytes // 4
+    stash = run.ws[lay.stash_offset:lay.stash_offset + B * Hq * lay.stash_row_bytes].view(torch.float32)
+    stash = stash.view(B, Hq, row)
+    s_gpu = {bh: stash[bh[0], bh[1]].double().cpu().numpy() for bh in heads}
+    santa.santa_sample_pass(*run.args(0))
+    torch.cuda.synchronize()
+    q, k, v, lens, bt = _oracle_arrays(run.copies[0])
+    res = O.decode(q, k, v, lens, bt, w.page_size, S, mode, w.sample_seed, heads=heads)
+    rep = dict(heads=0, targets=0, boundary_cases=0, boundary_mismatches=0, far_mismatches=0,
+               worst_rel_l2=0.0, max_abs_cdf_diff=0.0)
+    for (b, h), r in res.items():
+        n = int(r["n"])
+        if n == 0:
+            continue
+        rep["heads"] += 1
+        rep["targets"] += S
+        near = r["delta"] < BOUNDARY_WINDOW
+        bad = idx_gpu[b, h] != r["idx"]
+        rep["boundary_cases"] += int(near.sum())
+        rep["boundary_mismatches"] += int((bad & near).sum())
+        rep["far_mismatches"] += int((bad & ~near).sum())
+        g = h // w.group
+        vals = O.sequence_keys(v, n, b, bt, w.page_size)[:, g, :].astype(np.float64)
+        own = O.estimate(vals, idx_gpu[b, h])
+        rep["worst_rel_l2"] = max(rep["worst_rel_l2"], float(np.linalg.norm(o_gpu[b, h] - own) /
+                                                             max(np.linalg.norm(own), 1e-30)))
+        F_gpu = O.cdf(O.softmax(s_gpu[(b, h)][:n]))
+        rep["max_abs_cdf_diff"] = max(rep["max_abs_cdf_diff"], float(np.abs(F_gpu - r["F"]).max()))
+    return rep
+
+
+def cpu_baseline(w, x, S, mode, seconds):
+    """The oracle on the host, one BLAS thread: full decode steps of the same
+    workload (all heads), repeated until about `seconds` of CPU time."""
+    from threadpoolctl import threadpool_limits
+    from oracle import santa as O
+    q, k, v, lens, bt = _oracle_arrays(x)
     heads = [(b, h) for b in range(w.batch) for h in range(w.q_heads)]
-    # bounded sample: whole steps if they fit in the budget, else a prefix of heads
     done_heads = 0
-    t0 = time.perf_counter()
-    while True:
-        for i in range(0, len(heads), w.group):
-            O.decode(q, k, v, lens, bt, w.page_size, S, mode, w.sample_seed, heads=heads[i:i + w.group])
-            done_heads += w.group
-            if time.perf_counter() - t0 > seconds and done_heads >= w.group:
-                break
-        if time.perf_counter() - t0 > seconds:
-            break
-    elapsed = time.perf_counter() - t0
-    return {"value": done_heads / elapsed, "unit": "heads×batch/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"{done_heads} query heads of the {w.name} workload (NumPy fp64 oracle, "
-                      f"{w.group} heads of one KV head per call) in {elapsed:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0))}
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 <= seconds:
+            for i in range(0, len(heads), w.group):
+                O.decode(q, k, v, lens, bt, w.page_size, S, mode, w.sample_seed, heads=heads[i:i + w.group])
+                done_heads += w.group
+                if time.perf_counter() - t0 > seconds:
+                    break
+        elapsed = time.perf_counter() - t0
+    return {"value": done_heads / elapsed, "unit": "heads×batch/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_heads} query heads of the {w.name} workload (NumPy fp64 oracle, one BLAS "
+                      f"thread, {w.group} heads of one KV head per call) in {elapsed:.1f} s",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def main():
-    args = parse()
+def step_record(santa, w, run, S, mode, t_step, rounds, calls):
+    """Algorithmic traffic of `run`'s step: all K plus the distinct sampled V rows of
+    each KV copy's call (their mean over the copies)."""
+    uniq = []
+    for c in range(len(run.copies)):
+        run.step(c)
+        torch.cuda.synchronize()
+        uniq.append(W.unique_v_rows(run.idx.cpu(), w.group))
+    lens = run.copies[0]["seq_lens"].cpu().tolist()
+    u = sum(uniq) / len(uniq)
+    alg = W.traffic_bytes(w, lens, int(round(u)))
+    return {"step_us": t_step * 1e6, "calls_timed": calls, "rounds": round_stats(rounds),
+            "algorithmic_bytes": alg, "unique_v_rows": u, "achieved_GBs": alg / t_step / 1e9,
+            "frac_of_peak": alg / t_step / 1e9 / PEAK_HBM_GBS,
+            "path": santa.santa_decode_path(run.shape, S, mode)}
+
+
+def qwen_line(santa, steps, eager, dev):
+    """The Qwen2.5-7B-shaped long-context step (one KV copy of 1 GiB: K alone is
+    twice the Infinity Cache) for every sampling rule of the workload."""
+    w = W.WORKLOADS["qwen128k"]
+    S = w.samples[0]
+    copies = make_copies(w, 1, dev)
+    torch.cuda.synchronize()
+    out = {"config": {"batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                      "seq_len": w.seq_len, "samples": S, "kv_copies": 1}}
+    for mode in w.modes:
+        run = Runner(santa, copies, S, mode, 0)
+        for i in range(20):
+            run.step(i)
+        t, rounds, calls = timed(run.step, steps, eager, 1)
+        rec = step_record(santa, w, run, S, mode, t, rounds, calls)
+        rec["heads_x_batch_per_s"] = w.batch * w.q_heads / t
+        out[W.MODE_NAMES[mode]] = rec
+        del run
+    lens = copies[0]["seq_lens"].cpu().tolist()
+    out["dense_read_bytes"] = W.dense_read_bytes(w, lens)
+    out["dense_read_us_at_peak"] = out["dense_read_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e6
+    del copies
+    torch.cuda.empty_cache()
+    return out
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path.", file=sys.stderr)
@@ -263,7 +386,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
+        t, gbs = copy_bandwidth(args.calibrate_copy)
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "copy_us": t * 1e6,
+                          "read_plus_write_gbs": gbs}))
         return
     w = W.WORKLOADS[args.workload]
     S = args.samples or w.samples[0]
@@ -280,48 +405,47 @@ def main():
         run.step(i)
     torch.cuda.synchronize()
     print("[bench] timing steps", file=sys.stderr, flush=True)
-    t_step = timed(run.step, args.steps, args.eager, ncopies)
-    step_rounds = None if args.eager else round_stats(LAST_ROUNDS)
-    # the two-kernel path (score pass + sample pass), for comparison
-    t_two = timed(lambda c: (run.score(c), run.sample(c)), args.steps, args.eager, ncopies)
-    # S^2ANTA-flash (santa_decode_flash) on the same inputs, at this S and at the
-    # page's flash operating point S = 2048: reported beside the headline
-    flash = {}
-    if mode != W.MODE_MULTINOMIAL:
-        for S_f in sorted({S, 2048}):
-            if S_f < lay.num_splits:
-                continue
-            run_f = Runner(santa, copies, S_f, mode, args.split)
-            call = lambda c, r=run_f: santa.santa_decode_flash(*r._args(c))
-            t_f = timed(call, args.steps, args.eager, ncopies)
-            call(0)
-            torch.cuda.synchronize()
-            u_f = W.unique_v_rows(run_f.idx.cpu(), w.group)
-            b_f = W.traffic_bytes(w, copies[0]["seq_lens"].cpu().tolist(), u_f)
-            flash[f"S{S_f}"] = {"step_us": t_f * 1e6, "unique_v_rows": u_f, "algorithmic_bytes": b_f,
-                                "achieved_GBs": b_f / t_f / 1e9}
-            del run_f
+    t_step, rounds, calls = timed(run.step, args.steps, args.eager, ncopies)
+    head = step_record(santa, w, run, S, mode, t_step, rounds, calls)
+    lens = copies[0]["seq_lens"].cpu().tolist()
+    dense = W.dense_read_bytes(w, lens)
+    achieved = head["achieved_GBs"]
+    path = head["path"]
 
-    # algorithmic traffic of one step: all K rows + distinct sampled V rows
-    lens = copies[0]["seq_lens"].cpu()
-    uniq = []
-    for c in range(ncopies):
-        run.step(c)
-        torch.cuda.synchronize()
-        uniq.append(W.unique_v_rows(run.idx.cpu(), w.group))
-    uniq_mean = sum(uniq) / len(uniq)
-    alg_bytes = W.traffic_bytes(w, lens.tolist(), int(round(uniq_mean)))
-    dense = W.dense_read_bytes(w, lens.tolist())
-    achieved = alg_bytes / t_step / 1e9
-    traffic = counter_traffic(w.name)
-    path = santa.santa_decode_path(run.shape, S, mode)
+    extras = {}
+    if not args.no_extras:
+        print("[bench] timing the two-kernel path, flash, the Qwen step and a plain copy", file=sys.stderr,
+              flush=True)
+        side_steps = min(args.steps, 400)
+        t_two, r_two, c_two = timed(run.two_kernel, side_steps, args.eager, ncopies)
+        extras["two_kernel"] = {"step_us": t_two * 1e6, "calls_timed": c_two, "rounds": round_stats(r_two)}
+        flash = {}
+        if mode != W.MODE_MULTINOMIAL:
+            # S^2ANTA-flash on the same inputs, at this S and at the page's flash
+            # operating point S = 2048
+            for S_f in sorted({S, 2048}):
+                if S_f < lay.num_splits:
+                    continue
+                run_f = Runner(santa, copies, S_f, mode, args.split)
+                t_f, r_f, c_f = timed(run_f.flash, side_steps, args.eager, ncopies)
+                run_f.flash(0)
+                torch.cuda.synchronize()
+                u_f = W.unique_v_rows(run_f.idx.cpu(), w.group)
+                b_f = W.traffic_bytes(w, lens, u_f)
+                flash[f"S{S_f}"] = {"step_us": t_f * 1e6, "calls_timed": c_f, "unique_v_rows": u_f,
+                                    "algorithmic_bytes": b_f, "achieved_GBs": b_f / t_f / 1e9}
+                del run_f
+        extras["flash"] = flash
+        t_copy, copy_gbs = copy_bandwidth(1 << 30)
+        extras["copy"] = {"bytes": 1 << 30, "copy_us": t_copy * 1e6, "read_plus_write_GBs": copy_gbs,
+                          "frac_of_peak": copy_gbs / PEAK_HBM_GBS}
 
     rec = {
         "metric": METRIC,
         "value": w.batch * w.q_heads / t_step,
         "unit": "heads×batch/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": calls,
         "warmup": args.warmup,
         "ms_per_step": t_step * 1e3,
         "higher_is_better": True,
@@ -334,19 +458,34 @@ def main():
                    "mode": W.MODE_NAMES[mode], "split_size": lay.split_size,
                    "kv_copies": ncopies, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": {"bound": "hbm",
-                     "kernel": "fused_kernel" if path == santa.PATH_FUSED else "score+sample",
+                     "kernel": "fused_kernel" if path == santa.PATH_FUSED else "score_kernel+sample_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "bytes_per_launch": alg_bytes, "avg_launch_us": t_step * 1e6},
-        "step": {"decode_us": t_step * 1e6, "decode_rounds": step_rounds, "decode_path": path,
-                 "two_kernel_step_us": t_two * 1e6, "flash": flash,
-                 "algorithmic_bytes": alg_bytes, "k_bytes": int(lens.sum()) * w.kv_heads * w.head_dim * w.elem_bytes,
-                 "unique_v_rows": uniq_mean, "dense_read_bytes": dense,
-                 "dense_read_us_at_peak": dense / (PEAK_HBM_GBS * 1e9) * 1e6},
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": counter_traffic(w.name),
+                     "bytes_per_launch": head["algorithmic_bytes"], "avg_launch_us": t_step * 1e6},
+        "step": {"decode_us": t_step * 1e6, "decode_rounds": head["rounds"], "decode_path": path,
+                 "algorithmic_bytes": head["algorithmic_bytes"],
+                 "k_bytes": int(sum(lens)) * w.kv_heads * w.head_dim * w.elem_bytes,
+                 "unique_v_rows": head["unique_v_rows"], "dense_read_bytes": dense,
+                 "dense_read_us_at_peak": dense / (PEAK_HBM_GBS * 1e9) * 1e6, **extras},
+        "parity": None,
         "cpu_baseline": None,
     }
+    if "copy" in extras:
+        c = extras["copy"]["read_plus_write_GBs"]
+        rec["roofline"]["measured_copy_GBs"] = c
+        rec["roofline"]["frac_of_measured_copy"] = achieved / c
+        rec["step"]["dense_read_us_at_measured_copy"] = dense / (c * 1e9) * 1e6
+    if not args.no_extras and args.workload == "llama32k":
+        print("[bench] timing the Qwen-shaped step", file=sys.stderr, flush=True)
+        del copies, run
+        torch.cuda.empty_cache()
+        rec["qwen128k"] = qwen_line(santa, min(args.steps, 400), args.eager, dev)
+        copies = make_copies(w, 1, dev)
+        run = Runner(santa, copies, S, mode, args.split)
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        print("[bench] oracle: parity sample and CPU timing", file=sys.stderr, flush=True)
+        heads = [(b, h) for b in range(w.batch) for h in range(w.q_heads)][:64]
+        rec["parity"] = parity_sample(santa, run, w, S, mode, heads)
         rec["cpu_baseline"] = cpu_baseline(w, copies[0], S, mode, args.cpu_seconds)
     print(json.dumps(rec))
 

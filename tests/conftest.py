@@ -24,3 +24,25 @@ def gpu_available() -> bool:
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Writes the boundary-case counts and worst relative L2 of every GPU parity
+    configuration checked in this session to gpurun_out/parity_report.json."""
+    import json
+    import sys
+    helpers = sys.modules.get("tests.gpu_helpers")
+    reports = getattr(helpers, "SESSION_REPORTS", None) if helpers else None
+    if not reports:
+        return
+    out = os.path.join(ROOT, "gpurun_out")
+    os.makedirs(out, exist_ok=True)
+    total = dict(configs=len(reports), heads=0, targets=0, boundary_cases=0, boundary_mismatches=0,
+                 worst_rel_l2=0.0)
+    for r in reports.values():
+        for key in ("heads", "targets", "boundary_cases", "boundary_mismatches"):
+            total[key] += r[key]
+        total["worst_rel_l2"] = max(total["worst_rel_l2"], r["worst_rel_l2"])
+    with open(os.path.join(out, "parity_report.json"), "w") as f:
+        json.dump({"exit_status": int(exitstatus), "total": total, "by_config": reports}, f, indent=1,
+                  sort_keys=True)

@@ -63,6 +63,22 @@ def oracle_head(x: dict, b: int, h: int, S: int, mode: int, seed: int, rows=None
     return dict(idx=idx, t=t, F=F, p=p, s=s, v=v, delta=O.boundary_distance(F, idx, t))
 
 
+# Parity reports of this test session by configuration; tests/conftest.py writes
+# them to gpurun_out/parity_report.json when the session ends.
+SESSION_REPORTS = {}
+
+
+def record(label: str, rep: "ParityReport") -> None:
+    """Adds a report's counts to the session record of configuration `label`."""
+    r = SESSION_REPORTS.setdefault(label, dict(heads=0, targets=0, boundary_cases=0, boundary_mismatches=0,
+                                                worst_rel_l2=0.0))
+    r["heads"] += rep.heads
+    r["targets"] += rep.targets
+    r["boundary_cases"] += rep.boundary
+    r["boundary_mismatches"] += rep.boundary_mismatch
+    r["worst_rel_l2"] = max(r["worst_rel_l2"], rep.worst_rel_l2)
+
+
 class ParityReport:
     def __init__(self):
         self.heads = 0
@@ -102,8 +118,14 @@ def check_head(rep: ParityReport, ref: dict, idx_gpu: np.ndarray, o_gpu: np.ndar
     assert err <= O_REL_L2, f"{where}: o relative L2 error {err:.3e}"
 
 
+def _label(x: dict, S: int, mode: int, kind: str) -> str:
+    w = x["workload"]
+    return (f"{kind} {w.name} B{w.batch} {w.q_heads}/{w.kv_heads} d{w.head_dim} n{w.seq_len} {w.dtype}"
+            f"{' paged' + str(w.page_size) if w.page_size else ''} S{S} {W.MODE_NAMES[mode]}")
+
+
 def check_all(x: dict, S: int, mode: int, seed: int, o: torch.Tensor, idx: torch.Tensor,
-              heads=None) -> ParityReport:
+              heads=None, label=None) -> ParityReport:
     w = x["workload"]
     rep = ParityReport()
     lens = x["seq_lens"].cpu()
@@ -123,6 +145,7 @@ def check_all(x: dict, S: int, mode: int, seed: int, o: torch.Tensor, idx: torch
         ref = oracle_head(x, b, h, S, mode, seed, rows_cache[(b, g)])
         check_head(rep, ref, idx[b, h].numpy().astype(np.int64), o[b, h].double().numpy(),
                    f"(b={b}, h={h}, mode={mode}, S={S})")
+    record(label or _label(x, S, mode, "santa"), rep)
     return rep
 
 
@@ -142,7 +165,7 @@ def run_flash(x: dict, S: int, mode: int, seed: int, split: int = 0, workspace=N
 
 
 def check_flash(x: dict, S: int, mode: int, seed: int, tile: int, o: torch.Tensor, idx: torch.Tensor,
-                heads=None) -> ParityReport:
+                heads=None, label=None) -> ParityReport:
     """S^2ANTA-flash parity: idx exact outside the boundary window of each tile's local CDF;
     o within O_REL_L2 of the oracle's fp64 merge of the GPU's own idx."""
     w = x["workload"]
@@ -186,6 +209,7 @@ def check_flash(x: dict, S: int, mode: int, seed: int, tile: int, o: torch.Tenso
         err = float(np.linalg.norm(o[b, h].double().numpy() - own) / max(np.linalg.norm(own), 1e-30))
         rep.worst_rel_l2 = max(rep.worst_rel_l2, err)
         assert err <= O_REL_L2, f"{where}: o relative L2 error {err:.3e}"
+    record(label or _label(x, S, mode, f"flash tile{tile}"), rep)
     return rep
 
 

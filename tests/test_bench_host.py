@@ -55,3 +55,28 @@ def test_source_hash_ignores_comments_but_not_code():
     changed = dict(src)
     changed[first] = src[first] + "\nstatic int added_symbol = 1;\n"
     assert bench.kernel_source_hash(lambda n: changed[n]) != base
+
+
+@pytest.mark.parametrize("steps", [1, 7, 10, 20, 97, 200, 400, 2000, 4000])
+@pytest.mark.parametrize("ncopies", [1, 3, 8])
+def test_graph_plan_times_exactly_the_requested_calls(steps, ncopies):
+    L, P, replays, rounds = bench.graph_plan(steps, ncopies)
+    assert L * replays == steps                         # exactly --steps calls
+    assert 1 <= L <= bench.MAX_GRAPH_CALLS
+    assert rounds <= replays
+    assert rounds >= min(10, steps)                     # the driver's --steps 20 still has 10 rounds
+    # graph j replays calls j*L .. j*L+L-1; P graphs bring the KV copy back to where graph 0 starts
+    assert (P * L) % ncopies == 0 and all((j * L) % ncopies != 0 for j in range(1, P))
+
+
+def test_graph_plan_uses_full_graphs_for_long_runs():
+    L, P, replays, rounds = bench.graph_plan(4000, 8)
+    assert (L, rounds) == (32, 20) and replays == 125
+    assert bench.graph_plan(20, 8)[:1] == (2,)
+
+
+def test_gpus_above_one_exit_with_a_message(capsys):
+    with pytest.raises(SystemExit) as e:
+        bench.main(["--gpus", "2"])
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err

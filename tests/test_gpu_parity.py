@@ -427,3 +427,26 @@ def test_args_entry_point_and_forced_two_kernel_path(mode):
         santa.santa_decode_flash(shape, x["q"], x["k"], x["v"], x["seq_lens"], None, S, mode, 21, o, i2, ws)
         torch.cuda.synchronize()
         assert torch.equal(i1.cpu(), i2.cpu())
+
+
+@pytest.mark.parametrize("dtype,d,n,split", [("f32", 64, 1024, 0), ("bf16", 128, 4096, 0), ("bf16", 128, 3000, 256)])
+def test_systematic_full_budget_uniform_scores_is_exact(dtype, d, n, split):
+    """q = 0 makes every score 0, so p_i = 1/n exactly; systematic sampling with S = n
+    then puts target m in key m's interval (the SANTA page, section 2.1 Construction):
+    idx = 0 .. n-1 in order, and o = mean(V).  The offset is kept away from the
+    interval edges, so no target is a boundary case."""
+    w = W.Workload("uniform", batch=1, q_heads=4, kv_heads=1, head_dim=d, seq_len=n, dtype=dtype)
+    x = W.make_inputs(w, seed=5)
+    x["q"] = torch.zeros_like(x["q"])
+    x = H.to_device(x)
+    seed = next(s for s in range(100) if 0.01 < float(O.uniforms(s, 0, 0, [0])[0]) < 0.99 and
+                all(0.01 < float(O.uniforms(s, 0, h, [0])[0]) < 0.99 for h in range(4)))
+    print(f"[case] uniform scores {dtype} d={d} n={n} split={split} seed={seed}", flush=True)
+    o, idx, ws, shape = H.run_hip(x, n, W.MODE_SYSTEMATIC, seed=seed, split=split)
+    assert santa.santa_workspace_status(ws) == 0
+    v = x["v"][0, :n, 0].double().cpu()
+    for h in range(4):
+        assert torch.equal(idx[0, h], torch.arange(n, dtype=torch.int32)), h
+        err = float((o[0, h].double() - v.mean(0)).norm() / v.mean(0).norm())
+        assert err < 1e-5, (h, err)
+    H.check_all(x, n, W.MODE_SYSTEMATIC, seed, o, idx)
