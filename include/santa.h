@@ -334,6 +334,45 @@ santa_status santa_decode_args(const santa_args* args, void* stream);
 santa_status santa_workspace_status(const void* workspace, size_t workspace_bytes, void* stream,
                                     uint32_t* error_word);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): santa_decode
+ * without a workspace argument.  Its workspace is a 64 MiB array that is part
+ * of the library's code object (SANTA_NOALLOC_SCRATCH_BYTES, held by every
+ * device the library runs on until the process ends); these calls allocate
+ * nothing.  Everything else is santa_decode's: the same kernels, path choice,
+ * arguments (minus workspace and workspace_bytes) and results.
+ *
+ *   - A problem whose santa_workspace_size exceeds the array returns
+ *     SANTA_STATUS_WORKSPACE_TOO_SMALL before touching the device (the
+ *     Llama-3.1-8B-shaped 32k step needs 4.3 MiB; batch 4 of 28/4 heads at
+ *     128k tokens about 60 MiB).
+ *   - All calls on one device share that device's array, and its state
+ *     carries from call to call exactly as santa_decode's workspace does: a
+ *     completed call leaves it zero.  Calls that overlap on one device (two
+ *     streams, two threads without ordering) race on it; order them.
+ *   - The array must be zero before the first call: santa_noalloc_init clears
+ *     it on `stream` (call it once per device before capturing a graph, and
+ *     again after santa_noalloc_status reports a failed wait); otherwise the
+ *     first santa_decode_noalloc on a device enqueues that clear itself.
+ */
+#define SANTA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* Bytes of the no-allocation scratch array (SANTA_NOALLOC_SCRATCH_BYTES). */
+size_t santa_noalloc_scratch_bytes(void);
+
+/* Zero-fills the current device's scratch array on `stream` (a kernel, no allocation). */
+santa_status santa_noalloc_init(void* stream);
+
+/* santa_decode on the current device's scratch array (see above). */
+santa_status santa_decode_noalloc(const santa_shape* shape, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                                  int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                                  void* stream);
+
+/* santa_workspace_status of the current device's scratch array (synchronises `stream`). */
+santa_status santa_noalloc_status(void* stream, uint32_t* error_word);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ __all__ = [
     "santa_workspace_size", "santa_workspace_init", "santa_decode_path", "santa_decode",
     "santa_score_pass", "santa_sample_pass", "santa_decode_flash", "decode", "allocate_workspace",
     "workspace_error", "validate", "Args", "santa_decode_args", "santa_workspace_status",
-    "ALGO_PROP", "ALGO_FLASH", "FLAG_TWO_KERNEL",
+    "ALGO_PROP", "ALGO_FLASH", "FLAG_TWO_KERNEL", "santa_decode_noalloc", "santa_noalloc_init",
+    "santa_noalloc_status", "santa_noalloc_scratch_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "santa_workspace_layout_query", "santa_workspace_size", "santa_workspace_init",
     "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash",
     "santa_decode_args", "santa_workspace_status",
+    "santa_noalloc_scratch_bytes", "santa_noalloc_init", "santa_decode_noalloc", "santa_noalloc_status",
 )
 ALGO_PROP = 0
 ALGO_FLASH = 1
@@ -118,6 +120,14 @@ def library() -> ctypes.CDLL:
         lib.santa_decode_args.argtypes = [ctypes.POINTER(Args), vp]
         lib.santa_workspace_status.restype = ctypes.c_int
         lib.santa_workspace_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
+        lib.santa_noalloc_scratch_bytes.restype = sz
+        lib.santa_noalloc_scratch_bytes.argtypes = []
+        lib.santa_noalloc_init.restype = ctypes.c_int
+        lib.santa_noalloc_init.argtypes = [vp]
+        lib.santa_noalloc_status.restype = ctypes.c_int
+        lib.santa_noalloc_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+        lib.santa_decode_noalloc.restype = ctypes.c_int
+        lib.santa_decode_noalloc.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp]
         for name in ("santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
@@ -215,8 +225,9 @@ def validate(shape: Shape, q, k_cache, v_cache, seq_lens, block_table, num_sampl
         if not cond:
             raise ValueError(msg)
 
-    tensors = {"q": q, "k_cache": k_cache, "v_cache": v_cache, "seq_lens": seq_lens, "o": o, "idx": idx,
-               "workspace": workspace}
+    tensors = {"q": q, "k_cache": k_cache, "v_cache": v_cache, "seq_lens": seq_lens, "o": o, "idx": idx}
+    if workspace is not None:
+        tensors["workspace"] = workspace
     if block_table is not None:
         tensors["block_table"] = block_table
     for name, t in tensors.items():
@@ -264,7 +275,7 @@ def validate(shape: Shape, q, k_cache, v_cache, seq_lens, block_table, num_sampl
          "o must be a contiguous float32 [B, Hq, d] tensor")
     need(idx.dtype == torch.int32 and tuple(idx.shape) == (B, Hq, num_samples) and idx.is_contiguous(),
          f"idx must be a contiguous int32 [B, Hq, {num_samples}] tensor")
-    need(workspace.is_contiguous(), "workspace must be contiguous")
+    need(workspace is None or workspace.is_contiguous(), "workspace must be contiguous")
 
 
 def _call(name, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o, idx,
@@ -308,6 +319,34 @@ def santa_workspace_status(workspace: torch.Tensor, stream=None) -> int:
     out = ctypes.c_uint32()
     _check(library().santa_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream_handle(stream), ctypes.byref(out)), "santa_workspace_status")
+    return out.value
+
+
+def santa_noalloc_scratch_bytes() -> int:
+    """Bytes of the library's no-allocation scratch array."""
+    return int(library().santa_noalloc_scratch_bytes())
+
+
+def santa_noalloc_init(stream=None) -> None:
+    """Zero-fills the current device's scratch array (``santa_noalloc_init``)."""
+    _check(library().santa_noalloc_init(_stream_handle(stream)), "santa_noalloc_init")
+
+
+def santa_decode_noalloc(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o, idx,
+                         stream=None) -> None:
+    """``santa_decode`` on the library's own scratch array, allocating nothing
+    (``santa_decode_noalloc`` of the C ABI)."""
+    validate(shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, o, idx, None)
+    _check(library().santa_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(seq_lens), _ptr(block_table), int(num_samples), int(mode),
+                                          ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(o), _ptr(idx),
+                                          _stream_handle(stream)), "santa_decode_noalloc")
+
+
+def santa_noalloc_status(stream=None) -> int:
+    """The error word of the current device's scratch array (synchronises the stream)."""
+    out = ctypes.c_uint32()
+    _check(library().santa_noalloc_status(_stream_handle(stream), ctypes.byref(out)), "santa_noalloc_status")
     return out.value
 
 

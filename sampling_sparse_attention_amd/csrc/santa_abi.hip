@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "santa.h"
 #include "santa_internal.h"
 
@@ -262,9 +264,98 @@ santa_status run(int stages, const santa_shape* s, const void* q, const void* k,
     return SANTA_STATUS_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The workspace of santa_decode_noalloc: one array per device, a part of the
+// library's code object (no allocation call).  In host code `scratch` only
+// names the symbol; its device address comes from hipGetSymbolAddress, once
+// per device, and is what every kernel and the clear receive.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocBytes = SANTA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};     // device address of `scratch` per device
+bool g_scratch_clear[kMaxDevices] = {};    // its zero fill has been enqueued
+
+// The current device's scratch address, looked up once per device; with
+// `clear`, the first call on a device also enqueues its zero fill on `stream`
+// (the workspace protocol needs all zero before a first call).
+santa_status noalloc_scratch(bool clear, hipStream_t stream, void** out) {
+    int dev = 0;
+    santa_status st = hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st != SANTA_STATUS_OK) return st;
+    if (dev < 0 || dev >= kMaxDevices) return fail(SANTA_STATUS_UNSUPPORTED, "device %d above %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        st = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (st != SANTA_STATUS_OK) return st;
+        if (!ptr || !aligned(ptr, 256))
+            return fail(SANTA_STATUS_HIP_ERROR, "the scratch array has no usable device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    if (clear && !g_scratch_clear[dev]) {
+        st = hip_check(santa::launch_clear(g_scratch_ptr[dev], kNoAllocBytes, stream), "clearing the scratch array");
+        if (st != SANTA_STATUS_OK) return st;
+        g_scratch_clear[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return SANTA_STATUS_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t santa_noalloc_scratch_bytes(void) { return kNoAllocBytes; }
+
+santa_status santa_noalloc_init(void* stream) {
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    void* ptr = nullptr;
+    santa_status st = noalloc_scratch(false, hs, &ptr);
+    if (st != SANTA_STATUS_OK) return st;
+    st = hip_check(santa::launch_clear(ptr, kNoAllocBytes, hs), "clearing the scratch array");
+    if (st != SANTA_STATUS_OK) return st;
+    {
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            g_scratch_clear[dev] = true;
+        }
+    }
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_decode_noalloc(const santa_shape* shape, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                                  int32_t num_samples, int32_t mode, uint64_t seed, float* o, int32_t* idx,
+                                  void* stream) {
+    // the size check first, so that a problem too large is refused before the
+    // device is touched
+    Plan plan;
+    santa_status st = make_plan(shape, num_samples, mode, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    if (plan.layout.total_bytes > kNoAllocBytes)
+        return fail(SANTA_STATUS_WORKSPACE_TOO_SMALL,
+                    "santa_decode_noalloc: the problem needs %zu bytes of workspace, the scratch array holds %zu "
+                    "(use santa_decode with a workspace)",
+                    plan.layout.total_bytes, kNoAllocBytes);
+    void* ws = nullptr;
+    st = noalloc_scratch(true, static_cast<hipStream_t>(stream), &ws);
+    if (st != SANTA_STATUS_OK) return st;
+    return run(kDecode, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed, o, idx, ws,
+               kNoAllocBytes, stream);
+}
+
+santa_status santa_noalloc_status(void* stream, uint32_t* error_word) {
+    void* ws = nullptr;
+    santa_status st = noalloc_scratch(false, static_cast<hipStream_t>(stream), &ws);
+    if (st != SANTA_STATUS_OK) return st;
+    return santa_workspace_status(ws, kNoAllocBytes, stream, error_word);
+}
+
 
 int32_t santa_abi_version(void) { return SANTA_ABI_VERSION; }
 

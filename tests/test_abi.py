@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert len(declared) == 13
+    assert len(declared) == 17
     out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (santa_\w+)", out))
@@ -255,3 +255,16 @@ def test_workspace_status_validates_before_touching_the_device(lib):
     assert lib.santa_workspace_status(ctypes.c_void_p((1 << 20) + 4), 4096, None, ctypes.byref(word)) == INVALID
     assert lib.santa_workspace_status(ctypes.c_void_p(1 << 20), 16, None, ctypes.byref(word)) == WS_SMALL
     assert word.value == 7
+
+
+def test_noalloc_refuses_oversized_problems_before_touching_the_device(lib):
+    assert lib.santa_noalloc_scratch_bytes() == 64 << 20
+    paged = _shape(batch=64, max_seq_len=32768, page_size=16, pages_per_seq=2048, num_pages=131072,
+                   kv_stride_seq=16 * 8 * 128)
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.santa_decode_noalloc(ctypes.byref(paged), fake, fake, fake, fake, fake, 256, 2, ctypes.c_uint64(0),
+                                  fake, fake, None)
+    assert st == WS_SMALL
+    assert "scratch array holds" in lib.santa_last_error().decode()
+    assert lib.santa_decode_noalloc(ctypes.byref(_shape(head_dim=96)), fake, fake, fake, fake, None, 64, 2,
+                                    ctypes.c_uint64(0), fake, fake, None) == UNSUPPORTED
