@@ -458,7 +458,7 @@ def main(argv=None):
                    "mode": W.MODE_NAMES[mode], "split_size": lay.split_size,
                    "kv_copies": ncopies, "launch": "eager" if args.eager else "hip_graph"},
         "roofline": {"bound": "hbm",
-                     "kernel": "fused_kernel" if path == santa.PATH_FUSED else "score_kernel+sample_kernel",
+                     "kernel": "score_kernel+sample_kernel" if path == santa.PATH_TWO_KERNELS else "fused_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": counter_traffic(w.name),
                      "bytes_per_launch": head["algorithmic_bytes"], "avg_launch_us": t_step * 1e6},

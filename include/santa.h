@@ -60,10 +60,11 @@
  * reads the word; it is the authoritative signal that a call's outputs are
  * invalid (a group whose own splits did not wait may still hold finite values).
  *
- * Device residency: santa_decode's fused path (santa_decode_path() == 1) has
- * the workgroups of one (sequence, KV head) wait for each other, which is
- * safe only while the device holds every workgroup of the launch at once.
- * The library checks that from the occupancy of an otherwise idle device.  A
+ * Device residency: santa_decode's fused paths (santa_decode_path() == 1 or 3)
+ * have the workgroups of one (sequence, KV head) wait for each other, which is
+ * safe only while the device can hold every workgroup of the launch (path 1),
+ * or every workgroup of one group (path 3), at once.  The library checks
+ * that from the occupancy of an otherwise idle device.  A
  * kernel running on the same device at the same time (another stream, another
  * process) can keep workgroups from being placed until the waits give up.
  * Callers that share the device with concurrent kernels pass
@@ -136,7 +137,8 @@ typedef struct santa_shape {
  * Workspace layout (byte offsets into the caller's workspace, 256-byte aligned):
  *   sync     barrier_offset bytes at the start: a 32-bit error word (byte 0)
  *            that becomes nonzero if a bounded wait of a call gave up (that
- *            call's outputs are invalid; santa_workspace_init clears it);
+ *            call's outputs are invalid; santa_workspace_init clears it), and
+ *            at byte 128 the item counter of the fused kernel's path 3;
  *   barrier  [B, Hkv] x 18 lines of 128 bytes: per (sequence, KV head) the
  *            counts of its splits that have published their records and that
  *            have added their output in the current call, and 16 copies of a
@@ -203,9 +205,11 @@ santa_status santa_workspace_init(void* workspace, size_t workspace_bytes, void*
  * How santa_decode will run this problem on the current device: 1 = one fused
  * kernel (score pass, global budget and gather in one launch), used when the
  * device holds one workgroup per work item (sequence, KV head, split) at
- * once; 2 = the score pass followed by the sample pass otherwise.  Returns
- * the negated santa_status on error.  Queries the HIP runtime, touches no
- * memory.
+ * once; 3 = the same fused kernel when only the splits of one (sequence, KV
+ * head) fit at once: workgroups then take their work items from a counter in
+ * the workspace in the order they start, group by group; 2 = the score pass
+ * followed by the sample pass otherwise.  Returns the negated santa_status on
+ * error.  Queries the HIP runtime, touches no memory.
  */
 int32_t santa_decode_path(const santa_shape* shape, int32_t num_samples, int32_t mode);
 

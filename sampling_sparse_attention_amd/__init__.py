@@ -44,6 +44,7 @@ ALGO_FLASH = 1
 FLAG_TWO_KERNEL = 1
 PATH_FUSED = 1
 PATH_TWO_KERNELS = 2
+PATH_FUSED_TICKETS = 3
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG_DIR, "libsanta.so")
@@ -185,7 +186,9 @@ def santa_workspace_init(workspace: torch.Tensor, stream=None) -> None:
 
 
 def santa_decode_path(shape: Shape, num_samples: int, mode: int) -> int:
-    """1: ``santa_decode`` runs one fused kernel; 2: the score pass then the sample pass."""
+    """1: ``santa_decode`` runs one fused kernel with every workgroup resident; 3: the fused
+    kernel with items taken in start order (one group resident at a time); 2: the score
+    pass then the sample pass."""
     r = library().santa_decode_path(ctypes.byref(shape), num_samples, mode)
     if r < 0:
         _check(-r, "santa_decode_path")

@@ -203,6 +203,7 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->T = plan->T;
     p->items = (int32_t)((int64_t)s->batch * s->num_kv_heads * plan->T);
     p->item_order = santa::kOrderSplitFastest;
+    p->use_ticket = 0;
     p->S = S;
     p->mode = mode;
     return SANTA_STATUS_OK;
@@ -213,16 +214,20 @@ santa_status hip_check(hipError_t e, const char* what) {
     return fail(SANTA_STATUS_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
 }
 
-// How santa_decode runs a problem: 1 = the fused kernel, 2 = score pass +
-// sample pass, 0 = unknown (HIP error).  The fused kernel's workgroups wait for
-// one another, so it runs only when the device holds all of them at once.
+// How santa_decode runs a problem: 1 = the fused kernel, every workgroup
+// resident at once; 3 = the fused kernel with tickets (items taken in start
+// order, one group's splits resident at once); 2 = score pass + sample pass;
+// 0 = unknown (HIP error).  The fused kernel's workgroups wait for the other
+// splits of their group, so it needs room for a whole group on the device.
 int choose_path(const santa::Params& p, int dtype) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     const int per_cu = santa::fused_blocks_per_cu(p, dtype);
     if (per_cu <= 0) return 0;
-    return (int64_t)per_cu * cus >= (int64_t)p.items ? 1 : 2;
+    const int64_t slots = (int64_t)per_cu * cus;
+    if (slots >= (int64_t)p.items) return 1;
+    return slots >= (int64_t)p.T ? 3 : 2;
 }
 
 enum Stage { kScore = 1, kSample = 2, kDecode = 3 };
@@ -246,8 +251,13 @@ santa_status run(int stages, const santa_shape* s, const void* q, const void* k,
         st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
         if (st != SANTA_STATUS_OK) return st;
     }
-    if (path == 1) {
-        p.item_order = p.T % 8 == 0 ? santa::kOrderTokenBlocks : santa::kOrderHeadFastest;
+    if (path == 1 || path == 3) {
+        if (path == 1) {
+            p.item_order = p.T % 8 == 0 ? santa::kOrderTokenBlocks : santa::kOrderHeadFastest;
+        } else {
+            p.item_order = santa::kOrderSplitFastest;     // group by group, in ticket order
+            p.use_ticket = 1;
+        }
         st = hip_check(santa::launch_fused(p, s->dtype, hs), "launching the fused decode kernel");
         if (st != SANTA_STATUS_OK) return st;
     } else {

@@ -5,9 +5,18 @@
 // step.
 //
 // The only wait is for the statistics of the other splits of the same
-// sequence.  The host launches this kernel only when the device holds every
-// workgroup of the grid at once, so every statistic a workgroup waits for is
-// computed by a running workgroup.
+// (sequence, KV head) group.  Two ways to guarantee that every statistic a
+// workgroup waits for is computed by a workgroup that runs:
+//   - the device holds every workgroup of the grid at once (blockIdx gives
+//     the item);
+//   - tickets: each workgroup takes the next item from an atomic counter when
+//     it starts, items numbered group by group.  A workgroup then waits only
+//     for later tickets of its own group; once a ticket of the next group has
+//     been taken every ticket of this group has been, so the workgroups that
+//     hold slots are either of earlier groups, which finish without waiting
+//     for this one, or of this group.  A group needs at most as many slots as
+//     the device holds; the groups' K streams and latency-bound tails then
+//     overlap from one group to the next.
 #include "santa_split.h"
 
 namespace santa {
@@ -57,12 +66,32 @@ template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
 void fused_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const Item at = item_coords(p, blockIdx.x);
+    int item = blockIdx.x;
+    if (p.use_ticket) {
+        __shared__ int s_item;
+        if (threadIdx.x == 0) {
+            const unsigned int k =
+                __hip_atomic_fetch_add(&p.sync->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the last ticket of the launch: every other one has been taken, so
+            // the counter can return to zero for the next call
+            if (k == (unsigned int)p.items - 1u)
+                __hip_atomic_store(&p.sync->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // a counter that did not start at zero (a workspace never cleared):
+            // no item, and the call is marked failed
+            if (k >= (unsigned int)p.items)
+                __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_item = k < (unsigned int)p.items ? (int)k : -1;
+        }
+        __syncthreads();
+        item = s_item;
+        if (item < 0) return;
+    }
+    const Item at = item_coords(p, item);
     uint4 qf[G];
     priority_streaming();
     load_q<G, D, E, NT>(p, at.b, at.g, qf);
     const unsigned int err0 = p.sync->error;    // in flight with q, used after the K stream
-    fused_item<G, D, E, NT>(p, make_item(p, blockIdx.x), qf, err0, smem);
+    fused_item<G, D, E, NT>(p, make_item(p, item), qf, err0, smem);
 }
 
 template <int G, int D, typename E>

@@ -23,7 +23,9 @@ constexpr int kSpinLimit = 1 << 21;      // polls of a bounded wait (about 1 us 
 // written by the current call.
 struct SyncWords {
     unsigned int error;
-    unsigned int pad[63];
+    unsigned int pad0[31];
+    unsigned int ticket;          // fused kernel with tickets: items handed out so far this call
+    unsigned int pad1[31];
 };
 constexpr size_t kSyncBytes = sizeof(SyncWords);
 
@@ -82,6 +84,7 @@ struct Params {
     int32_t T;                    // splits per sequence: ceil(n_max / split)
     int32_t items;                // B * Hkv * T work items (one workgroup each)
     int32_t item_order;           // kOrder*: how a workgroup index maps to (b, g, t)
+    int32_t use_ticket;           // fused kernel: items taken in start order from sync->ticket
     int32_t S;
     int32_t mode;
 };

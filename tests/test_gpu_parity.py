@@ -211,16 +211,17 @@ def test_fused_and_two_kernel_paths_agree():
 
 
 def test_large_grid_repeated_calls_match_split_stages_and_oracle():
-    """A step with more work items than the device holds at once (two-kernel path):
-    the same indices as calling the score and sample passes directly, parity with the
-    oracle, and a workspace left all zero after several calls in a row."""
+    """A step with more work items than the device holds at once (the fused kernel
+    with tickets): the same indices as calling the score and sample passes directly,
+    parity with the oracle, and a workspace left all zero (ticket counter included)
+    after several calls in a row."""
     lens = (8192, 8000, 5000, 1, 0, 8191, 4096, 7777)
     x = _inputs(lens=lens, seed=9)
     S, split = 128, 64
     shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len, split_size=split)
     B, Hq, d = x["q"].shape
     for mode in (0, 1, 2):
-        assert santa.santa_decode_path(shape, S, mode) == santa.PATH_TWO_KERNELS
+        assert santa.santa_decode_path(shape, S, mode) == santa.PATH_FUSED_TICKETS
         ws = santa.allocate_workspace(shape, S, mode, "cuda")
         for seed in (5, 6, 7):
             o1 = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
