@@ -62,9 +62,9 @@
  *
  * Device residency: santa_decode's fused paths (santa_decode_path() == 1 or 3)
  * have the workgroups of one (sequence, KV head) wait for each other, which is
- * safe only while the device can hold every workgroup of the launch (path 1),
- * or every workgroup of one group (path 3), at once.  The library checks
- * that from the occupancy of an otherwise idle device.  A
+ * safe only while the device can hold every workgroup of the launch at once
+ * (path 1), or every workgroup of one group on each compute die (path 3).
+ * The library checks that from the occupancy of an otherwise idle device.  A
  * kernel running on the same device at the same time (another stream, another
  * process) can keep workgroups from being placed until the waits give up.
  * Callers that share the device with concurrent kernels pass
@@ -206,8 +206,9 @@ santa_status santa_workspace_init(void* workspace, size_t workspace_bytes, void*
  * kernel (score pass, global budget and gather in one launch), used when the
  * device holds one workgroup per work item (sequence, KV head, split) at
  * once; 3 = the same fused kernel when only the splits of one (sequence, KV
- * head) fit at once: workgroups then take their work items from a counter in
- * the workspace in the order they start, group by group; 2 = the score pass
+ * head) fit at once on a single compute die (XCD): workgroups then take their
+ * work items from a counter in the workspace in the order they start, group
+ * by group; 2 = the score pass
  * followed by the sample pass otherwise.  Returns the negated santa_status on
  * error.  Queries the HIP runtime, touches no memory.
  */
@@ -349,7 +350,7 @@ santa_status santa_workspace_status(const void* workspace, size_t workspace_byte
  *
  *   - A problem whose santa_workspace_size exceeds the array returns
  *     SANTA_STATUS_WORKSPACE_TOO_SMALL before touching the device (the
- *     Llama-3.1-8B-shaped 32k step needs 4.3 MiB; batch 4 of 28/4 heads at
+ *     Llama-3.1-8B-shaped 32k step needs 4.8 MiB; batch 4 of 28/4 heads at
  *     128k tokens about 60 MiB).
  *   - All calls on one device share that device's array, and its state
  *     carries from call to call exactly as santa_decode's workspace does: a

@@ -35,9 +35,12 @@ bool split_fits(int G, int D, int split) {
 // keeps HBM busy), doubled while a sequence would need more than
 // kMaxSplitsPerSeq splits, and halved until the split's LDS fits.  Larger
 // splits mean fewer workgroups repeating the same cross-split work after the
-// K stream; measured on a batch-1, 8-KV-head, 32k-token step: 26.3 us at
-// 512 keys against 27.7 at 256 and 30.8 at 1024.  The rule reads only the
-// shape, so the workspace size does not depend on the device.
+// K stream.  Measured: batch-1, 32/8-head, 32k-token step 26.3 us at 512 keys
+// against 27.7 at 256 and 30.8 at 1024; 64 x 32/8 heads at 32k (fused kernel
+// with tickets) 931 us at 512 against 1252 at 256 and 970 at 1024; 4 x 28/4
+// heads at 128k (score and sample passes) 262 us at 512 against 340 at 256.
+// The rule reads only the shape, so the workspace size does not depend on the
+// device.
 constexpr int64_t kTargetItems = 512;
 
 int default_split(const santa_shape& s, int G) {
@@ -216,18 +219,18 @@ santa_status hip_check(hipError_t e, const char* what) {
 
 // How santa_decode runs a problem: 1 = the fused kernel, every workgroup
 // resident at once; 3 = the fused kernel with tickets (items taken in start
-// order, one group's splits resident at once); 2 = score pass + sample pass;
-// 0 = unknown (HIP error).  The fused kernel's workgroups wait for the other
-// splits of their group, so it needs room for a whole group on the device.
+// order), when one group's splits fit on a single compute die (XCD); 2 =
+// score pass + sample pass; 0 = unknown (HIP error).  The fused kernel's
+// workgroups wait for the other splits of their group.
 int choose_path(const santa::Params& p, int dtype) {
-    int dev = 0, cus = 0;
+    int dev = 0, cus = 0, xccs = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xccs < 1) xccs = 1;
     const int per_cu = santa::fused_blocks_per_cu(p, dtype);
     if (per_cu <= 0) return 0;
-    const int64_t slots = (int64_t)per_cu * cus;
-    if (slots >= (int64_t)p.items) return 1;
-    return slots >= (int64_t)p.T ? 3 : 2;
+    if ((int64_t)per_cu * cus >= (int64_t)p.items) return 1;
+    return (int64_t)per_cu * (cus / xccs) >= (int64_t)p.T ? 3 : 2;
 }
 
 enum Stage { kScore = 1, kSample = 2, kDecode = 3 };

@@ -10,18 +10,26 @@
 //   - the device holds every workgroup of the grid at once (blockIdx gives
 //     the item);
 //   - tickets: each workgroup takes the next item from an atomic counter when
-//     it starts, items numbered group by group.  A workgroup then waits only
-//     for later tickets of its own group; once a ticket of the next group has
-//     been taken every ticket of this group has been, so the workgroups that
-//     hold slots are either of earlier groups, which finish without waiting
-//     for this one, or of this group.  A group needs at most as many slots as
-//     the device holds; the groups' K streams and latency-bound tails then
-//     overlap from one group to the next.
+//     it starts, items numbered group by group, and one group's splits fit on
+//     any single compute die (XCD).  A workgroup waits only for items of its
+//     own group.  Once a ticket of the next group is taken, every ticket of
+//     this group has been, so a workgroup that cannot be placed is kept out
+//     only by workgroups of earlier groups, which finish without waiting for
+//     later ones, or of this group.  A die whose slots all hold waiting
+//     workgroups of one group would hold the whole group, so while tickets of
+//     a group remain untaken some die that still has workgroups to start has
+//     a slot that frees.  (Room for one group on the whole device is not
+//     enough: the die a workgroup runs on is fixed by its index, and when
+//     some dies run out of workgroups the remaining tickets can only be
+//     taken on dies that one group's waiting workgroups may fill.)  The
+//     groups' K streams and latency-bound tails then overlap from one group
+//     to the next.
 #include "santa_split.h"
 
 namespace santa {
 
-template <int G, int D, typename E, int NT>
+// KW, UL: the sampler's keys counted at once and V loads in flight per lane
+template <int G, int D, typename E, int NT, int KW = 4, int UL = 8>
 __device__ __forceinline__ void fused_item(const Params& p, const Item& it, const uint4 (&qf)[G],
                                            unsigned int err0, unsigned char* smem) {
     if (it.n == 0) {
@@ -56,12 +64,22 @@ __device__ __forceinline__ void fused_item(const Params& p, const Item& it, cons
         poison_group<G, D, NT>(p, it);      // the barrier's result is the same in every thread
         return;
     }
-    prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit, &s_fail);
+    prefix_and_sample<G, D, E, NT, KW, UL>(p, it, L, smem, kSpinLimit, &s_fail);
     finish_output<G, D, NT>(p, it, &s_fail);
 }
 
 // Four waves per SIMD (all 1024 splits of a batch-1, 8-KV-head, 32k-token
 // step resident at once) where that fits without spilling registers.
+template <int G, int D, typename E, int NT, int KW = 4, int UL = 8>
+__device__ __forceinline__ void fused_one(const Params& p, int item, unsigned char* smem) {
+    const Item at = item_coords(p, item);
+    uint4 qf[G];
+    priority_streaming();
+    load_q<G, D, E, NT>(p, at.b, at.g, qf);
+    const unsigned int err0 = p.sync->error;    // in flight with q, used after the K stream
+    fused_item<G, D, E, NT, KW, UL>(p, make_item(p, item), qf, err0, smem);
+}
+
 template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
 void fused_kernel(Params p) {
@@ -73,7 +91,7 @@ void fused_kernel(Params p) {
             const unsigned int k =
                 __hip_atomic_fetch_add(&p.sync->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // the last ticket of the launch: every other one has been taken, so
-            // the counter can return to zero for the next call
+            // the counter returns to zero for the next call
             if (k == (unsigned int)p.items - 1u)
                 __hip_atomic_store(&p.sync->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // a counter that did not start at zero (a workspace never cleared):
@@ -86,12 +104,7 @@ void fused_kernel(Params p) {
         item = s_item;
         if (item < 0) return;
     }
-    const Item at = item_coords(p, item);
-    uint4 qf[G];
-    priority_streaming();
-    load_q<G, D, E, NT>(p, at.b, at.g, qf);
-    const unsigned int err0 = p.sync->error;    // in flight with q, used after the K stream
-    fused_item<G, D, E, NT>(p, make_item(p, item), qf, err0, smem);
+    fused_one<G, D, E, NT>(p, item, smem);
 }
 
 template <int G, int D, typename E>

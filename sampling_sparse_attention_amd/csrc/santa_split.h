@@ -956,7 +956,7 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
 // and the head is skipped: nothing is computed from an incomplete set of
 // records.
 // ---------------------------------------------------------------------------
-template <int G, int D, typename E, int NT>
+template <int G, int D, typename E, int NT, int KW = 4, int UL = 8>
 __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
                                                   unsigned char* smem, int spin_limit, int* fail) {
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
@@ -1071,7 +1071,7 @@ __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& i
         if (st.m_hi > st.m_lo) {
             // into accumulation slot t mod 16 of the group
             float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D;
-            sample_head<G, D, E>(p, it, st, h, L, smem, [&](int col, const float* vals) {
+            sample_head<G, D, E, KW, UL>(p, it, st, h, L, smem, [&](int col, const float* vals) {
 #pragma unroll
                 for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, vals[e]);
             });
