@@ -158,6 +158,10 @@ class Runner:
     def flash(self, c):
         self.santa.santa_decode_flash(*self.args(c))
 
+    def topk(self, c):
+        a = self.args(c)
+        self.santa.santa_decode_topk(*a[:6], self.S, *a[9:])
+
 
 def graph_plan(steps: int, ncopies: int, rounds: int = ROUNDS):
     """How `steps` timed calls are replayed: (calls per graph L, graphs P, replays,
@@ -436,6 +440,16 @@ def main(argv=None):
                                     "algorithmic_bytes": b_f, "achieved_GBs": b_f / t_f / 1e9}
                 del run_f
         extras["flash"] = flash
+        # the deterministic top-k comparator at the matched budget k = S
+        run_k = Runner(santa, copies, S, W.MODE_SYSTEMATIC, args.split)
+        t_k, r_k, c_k = timed(run_k.topk, side_steps, args.eager, ncopies)
+        run_k.topk(0)
+        torch.cuda.synchronize()
+        u_k = W.unique_v_rows(run_k.idx.cpu(), w.group)
+        b_k = W.traffic_bytes(w, lens, u_k)
+        extras["topk"] = {"k": S, "step_us": t_k * 1e6, "calls_timed": c_k, "unique_v_rows": u_k,
+                          "algorithmic_bytes": b_k, "achieved_GBs": b_k / t_k / 1e9}
+        del run_k
         t_copy, copy_gbs = copy_bandwidth(1 << 30)
         extras["copy"] = {"bytes": 1 << 30, "copy_us": t_copy * 1e6, "read_plus_write_GBs": copy_gbs,
                           "frac_of_peak": copy_gbs / PEAK_HBM_GBS}

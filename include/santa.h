@@ -290,6 +290,25 @@ santa_status santa_sample_pass(const santa_shape* shape, const void* q, const vo
                                uint64_t seed, float* o, int32_t* idx, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Deterministic top-k attention, the biased comparator the SANTA page measures
+ * SANTA against at a matched budget k = S (section 3.4; section 6): the exact
+ * scores of every key (Eq. 1, the score pass), the min(k, n_b) keys with the
+ * largest scores (lower token index first among equal scores, found by a radix
+ * select on the score stash), and attention renormalised over them,
+ *     o = sum_{i kept} exp(s_i) v_i / sum_{i kept} exp(s_i).
+ * idx [B, Hq, k] lists the kept token positions in ascending order, padded
+ * with -1 when n_b < k; a sequence of length 0 gives o = 0.  Arguments as for
+ * santa_decode (k in place of num_samples, no mode or seed); the workspace is
+ * santa_workspace_size(shape, k, SANTA_MODE_SYSTEMATIC) bytes (its score
+ * stash is used and returned to zero).  1 <= k <= 8192 (else
+ * SANTA_STATUS_UNSUPPORTED).  Two launches: the score pass, then one
+ * workgroup per (sequence, query head).
+ */
+santa_status santa_decode_topk(const santa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, const int32_t* block_table, int32_t k, float* o,
+                               int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Algorithms of santa_args. */
 enum {
     SANTA_ALGO_PROP = 0,    /* santa_decode: exact global budget (section 3.2, S2ANTA-prop) */

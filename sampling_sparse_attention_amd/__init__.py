@@ -21,7 +21,7 @@ __all__ = [
     "santa_score_pass", "santa_sample_pass", "santa_decode_flash", "decode", "allocate_workspace",
     "workspace_error", "validate", "Args", "santa_decode_args", "santa_workspace_status",
     "ALGO_PROP", "ALGO_FLASH", "FLAG_TWO_KERNEL", "santa_decode_noalloc", "santa_noalloc_init",
-    "santa_noalloc_status", "santa_noalloc_scratch_bytes",
+    "santa_noalloc_status", "santa_noalloc_scratch_bytes", "santa_decode_topk",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash",
     "santa_decode_args", "santa_workspace_status",
     "santa_noalloc_scratch_bytes", "santa_noalloc_init", "santa_decode_noalloc", "santa_noalloc_status",
+    "santa_decode_topk",
 )
 ALGO_PROP = 0
 ALGO_FLASH = 1
@@ -121,6 +122,8 @@ def library() -> ctypes.CDLL:
         lib.santa_decode_args.argtypes = [ctypes.POINTER(Args), vp]
         lib.santa_workspace_status.restype = ctypes.c_int
         lib.santa_workspace_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
+        lib.santa_decode_topk.restype = ctypes.c_int
+        lib.santa_decode_topk.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.santa_noalloc_scratch_bytes.restype = sz
         lib.santa_noalloc_scratch_bytes.argtypes = []
         lib.santa_noalloc_init.restype = ctypes.c_int
@@ -323,6 +326,17 @@ def santa_workspace_status(workspace: torch.Tensor, stream=None) -> int:
     _check(library().santa_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream_handle(stream), ctypes.byref(out)), "santa_workspace_status")
     return out.value
+
+
+def santa_decode_topk(shape, q, k_cache, v_cache, seq_lens, block_table, k, o, idx, workspace,
+                      stream=None) -> None:
+    """Top-k attention at budget k (``santa_decode_topk`` of the C ABI); the workspace is
+    ``santa_workspace_size(shape, k, MODE_SYSTEMATIC)`` bytes."""
+    validate(shape, q, k_cache, v_cache, seq_lens, block_table, k, o, idx, workspace)
+    _check(library().santa_decode_topk(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                       _ptr(block_table), int(k), _ptr(o), _ptr(idx), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "santa_decode_topk")
 
 
 def santa_noalloc_scratch_bytes() -> int:

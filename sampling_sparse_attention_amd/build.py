@@ -21,7 +21,8 @@ LIB_NAME = "libsanta.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["santa_abi.hip", "santa_score.hip", "santa_sample.hip", "santa_fused.hip", "santa_flash.hip"]
+SOURCES = ["santa_abi.hip", "santa_score.hip", "santa_sample.hip", "santa_fused.hip", "santa_flash.hip",
+           "santa_topk.hip"]
 
 COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -473,6 +473,25 @@ santa_status santa_decode_flash(const santa_shape* shape, const void* q, const v
     return SANTA_STATUS_OK;
 }
 
+santa_status santa_decode_topk(const santa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, const int32_t* block_table, int32_t k, float* o,
+                               int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+    santa::Params p;
+    Plan plan;
+    santa_status st = make_params(shape, q, k_cache, v_cache, seq_lens, block_table, k, SANTA_MODE_SYSTEMATIC, 0,
+                                  o, idx, workspace, workspace_bytes, &p, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    if (k > santa::kMaxTopk)
+        return fail(SANTA_STATUS_UNSUPPORTED, "santa_decode_topk keeps at most %d keys (k = %d)", santa::kMaxTopk, k);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    st = hip_check(santa::launch_score(p, shape->dtype, hs, false), "launching the score pass");
+    if (st != SANTA_STATUS_OK) return st;
+    st = hip_check(santa::launch_topk(p, shape->dtype, hs), "launching the top-k selection");
+    if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
 santa_status santa_decode_args(const santa_args* a, void* stream) {
     if (!a) return fail(SANTA_STATUS_INVALID_ARGUMENT, "args is NULL");
     if (a->flags & ~(uint32_t)SANTA_FLAG_TWO_KERNEL)

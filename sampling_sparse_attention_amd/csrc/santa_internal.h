@@ -98,7 +98,10 @@ size_t sort_lds_bytes(int S);
 constexpr int kThreads = 256;
 
 hipError_t launch_targets(const Params& p, hipStream_t stream);
-hipError_t launch_score(const Params& p, int dtype, hipStream_t stream);
+// stats = false: scores to the stash only (no split statistics or records)
+hipError_t launch_score(const Params& p, int dtype, hipStream_t stream, bool stats = true);
+hipError_t launch_topk(const Params& p, int dtype, hipStream_t stream);
+constexpr int kMaxTopk = 8192;           // largest k of the top-k comparator
 hipError_t launch_sample(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_fused(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream);

@@ -14,7 +14,9 @@ size_t sort_lds_bytes(int S) {
     return (size_t)n * sizeof(uint64_t);
 }
 
-template <int G, int D, typename E, int NT>
+// STATS: also the split statistics and records (the sample pass needs them;
+// the top-k comparator reads only the stash).
+template <int G, int D, typename E, int NT, bool STATS>
 __global__ __launch_bounds__(NT) void score_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Item at = item_coords(p, blockIdx.x);
@@ -30,8 +32,10 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
         __syncthreads();
         stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
         __syncthreads();
-        split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
-        __syncthreads();
+        if constexpr (STATS) {
+            split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
+            __syncthreads();
+        }
         // the stash: scaled scores of the split, coalesced 16-byte stores
         constexpr int NW = NT / 64;
         const int lane = threadIdx.x & 63;
@@ -102,31 +106,38 @@ hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int G, int D, typename E>
+template <int G, int D, typename E, bool STATS>
 static hipError_t launch_score_t(const Params& p, hipStream_t stream) {
     const size_t lds = split_lds_bytes(G, D, p.split, kThreads);
-    const hipError_t e = allow_lds(reinterpret_cast<const void*>(&score_kernel<G, D, E, kThreads>), lds);
+    const void* fn = reinterpret_cast<const void*>(&score_kernel<G, D, E, kThreads, STATS>);
+    const hipError_t e = allow_lds(fn, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((score_kernel<G, D, E, kThreads>), dim3((unsigned)p.items), dim3(kThreads), lds, stream, p);
+    hipLaunchKernelGGL((score_kernel<G, D, E, kThreads, STATS>), dim3((unsigned)p.items), dim3(kThreads), lds,
+                       stream, p);
     return hipGetLastError();
 }
 
-template <int D, typename E>
+template <int D, typename E, bool STATS>
 static hipError_t launch_score_d(const Params& p, hipStream_t stream) {
     switch (p.G) {
-        case 1: return launch_score_t<1, D, E>(p, stream);
-        case 2: return launch_score_t<2, D, E>(p, stream);
-        case 4: return launch_score_t<4, D, E>(p, stream);
-        case 7: return launch_score_t<7, D, E>(p, stream);
-        case 8: return launch_score_t<8, D, E>(p, stream);
+        case 1: return launch_score_t<1, D, E, STATS>(p, stream);
+        case 2: return launch_score_t<2, D, E, STATS>(p, stream);
+        case 4: return launch_score_t<4, D, E, STATS>(p, stream);
+        case 7: return launch_score_t<7, D, E, STATS>(p, stream);
+        case 8: return launch_score_t<8, D, E, STATS>(p, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_score(const Params& p, int dtype, hipStream_t stream) {
-    if (dtype == 0) return p.D == 64 ? launch_score_d<64, Bf16>(p, stream)
-                                     : launch_score_d<128, Bf16>(p, stream);
-    return p.D == 64 ? launch_score_d<64, F32>(p, stream) : launch_score_d<128, F32>(p, stream);
+template <bool STATS>
+static hipError_t launch_score_s(const Params& p, int dtype, hipStream_t stream) {
+    if (dtype == 0) return p.D == 64 ? launch_score_d<64, Bf16, STATS>(p, stream)
+                                     : launch_score_d<128, Bf16, STATS>(p, stream);
+    return p.D == 64 ? launch_score_d<64, F32, STATS>(p, stream) : launch_score_d<128, F32, STATS>(p, stream);
+}
+
+hipError_t launch_score(const Params& p, int dtype, hipStream_t stream, bool stats) {
+    return stats ? launch_score_s<true>(p, dtype, stream) : launch_score_s<false>(p, dtype, stream);
 }
 
 hipError_t launch_targets(const Params& p, hipStream_t stream) {
