@@ -309,6 +309,46 @@ santa_status santa_decode_topk(const santa_shape* shape, const void* q, const vo
                                const int32_t* seq_lens, const int32_t* block_table, int32_t k, float* o,
                                int32_t* idx, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Layout of K transposed (channel-major), for santa_decode_bernoulli: element
+ * (sequence b, KV head g, feature i, token j) at
+ *   b * stride_seq + g * stride_head + i * stride_feat + j
+ * (tokens contiguous; every row 16-byte aligned; stride_feat >= max_seq_len).
+ */
+typedef struct santa_kt_layout {
+    int64_t stride_seq;
+    int64_t stride_head;
+    int64_t stride_feat;
+} santa_kt_layout;
+
+/*
+ * Bernoulli qK^T with the mean group query, combined with SANTA (section 5,
+ * Eq. 5; section 5.1, Eq. 6; section 5.3).  The scores are estimated rather
+ * than exact: for every (sequence b, KV head g) group,
+ *   m_i      = (1/G) sum_h |q_{h,i}|                 (the mean group query)
+ *   count_i  = #{n < B : (n + U_{i,n}) / B < m_i / max_j m_j}
+ *              (B stratified Bernoulli draws; U from Philox4x64-10 with key
+ *              (seed, 1) and counter (n, i, g, b); decided in fp64)
+ *   s_hat_hj = sum_i ((max_j m_j / B) count_i / m_i) q_{h,i} k_{j,i}
+ * and SANTA then samples from softmax(s_hat / sqrt(d)) exactly as
+ * santa_decode does (same num_samples, mode and seed conventions).  Only the
+ * features with count_i > 0 are read from K^T, so skipped features cost no
+ * bytes; feature_counts [B, Hkv, d] (uint8, device) receives count_i.
+ *
+ *   shape        sizes and the layout of v_cache (contiguous: page_size 0)
+ *   k_t, kt      K transposed and its layout (santa_kt_layout)
+ *   v_cache      token-major V as in santa_decode
+ *   num_bernoulli B, 1 <= B <= 64
+ * Workspace: santa_workspace_size(shape, num_samples, mode) bytes.  Runs the
+ * feature counts, then the fused kernel (or the score and sample passes)
+ * chosen as for santa_decode.
+ */
+santa_status santa_decode_bernoulli(const santa_shape* shape, const void* q, const void* k_t,
+                                    const santa_kt_layout* kt, const void* v_cache, const int32_t* seq_lens,
+                                    int32_t num_samples, int32_t mode, uint64_t seed, int32_t num_bernoulli,
+                                    float* o, int32_t* idx, uint8_t* feature_counts, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Algorithms of santa_args. */
 enum {
     SANTA_ALGO_PROP = 0,    /* santa_decode: exact global budget (section 3.2, S2ANTA-prop) */

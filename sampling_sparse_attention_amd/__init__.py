@@ -22,7 +22,7 @@ __all__ = [
     "workspace_error", "validate", "Args", "santa_decode_args", "santa_workspace_status",
     "ALGO_PROP", "ALGO_FLASH", "FLAG_TWO_KERNEL", "santa_decode_noalloc", "santa_noalloc_init",
     "santa_noalloc_status", "santa_noalloc_scratch_bytes", "santa_decode_topk",
-    "EXPORTED_SYMBOLS",
+    "KtLayout", "santa_decode_bernoulli", "EXPORTED_SYMBOLS",
 ]
 
 MODE_MULTINOMIAL = 0
@@ -38,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "santa_decode_path", "santa_decode", "santa_score_pass", "santa_sample_pass", "santa_decode_flash",
     "santa_decode_args", "santa_workspace_status",
     "santa_noalloc_scratch_bytes", "santa_noalloc_init", "santa_decode_noalloc", "santa_noalloc_status",
-    "santa_decode_topk",
+    "santa_decode_topk", "santa_decode_bernoulli",
 )
 ALGO_PROP = 0
 ALGO_FLASH = 1
@@ -87,6 +87,11 @@ class Args(ctypes.Structure):
     ]
 
 
+class KtLayout(ctypes.Structure):
+    """Mirror of ``santa_kt_layout``."""
+    _fields_ = [("stride_seq", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("stride_feat", ctypes.c_int64)]
+
+
 class SantaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: {detail} (status {status})")
@@ -125,6 +130,9 @@ def library() -> ctypes.CDLL:
         lib.santa_decode_topk.restype = ctypes.c_int
         lib.santa_decode_topk.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         lib.santa_noalloc_scratch_bytes.restype = sz
+        lib.santa_decode_bernoulli.restype = ctypes.c_int
+        lib.santa_decode_bernoulli.argtypes = [ctypes.POINTER(Shape), vp, vp, ctypes.POINTER(KtLayout), vp, vp,
+                                               i32, i32, u64, i32, vp, vp, vp, vp, sz, vp]
         lib.santa_noalloc_scratch_bytes.argtypes = []
         lib.santa_noalloc_init.restype = ctypes.c_int
         lib.santa_noalloc_init.argtypes = [vp]
@@ -337,6 +345,36 @@ def santa_decode_topk(shape, q, k_cache, v_cache, seq_lens, block_table, k, o, i
                                        _ptr(block_table), int(k), _ptr(o), _ptr(idx), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "santa_decode_topk")
+
+
+def santa_decode_bernoulli(shape, q, k_t, v_cache, seq_lens, num_samples, mode, seed, num_bernoulli, o, idx,
+                           feature_counts, workspace, stream=None) -> None:
+    """Bernoulli qK^T with the mean group query, then SANTA (``santa_decode_bernoulli``
+    of the C ABI).  ``k_t`` is K transposed, ``[B, Hkv, d, >= n_max]`` with tokens
+    contiguous; ``shape`` describes the contiguous token-major ``v_cache``;
+    ``feature_counts`` is a uint8 ``[B, Hkv, d]`` output."""
+    validate(shape, q, v_cache, v_cache, seq_lens, None, num_samples, o, idx, workspace)
+    B, Hq, d = q.shape
+    if not isinstance(k_t, torch.Tensor) or k_t.device != q.device or k_t.dtype != q.dtype:
+        raise ValueError("k_t must be a tensor of q's dtype on q's device")
+    if k_t.dim() != 4 or k_t.stride(-1) != 1:
+        raise ValueError("k_t must be a [B, Hkv, d, tokens] tensor with tokens contiguous")
+    if k_t.shape[0] < B or k_t.shape[1] != shape.num_kv_heads or k_t.shape[2] != d or \
+            k_t.shape[3] < shape.max_seq_len:
+        raise ValueError(f"k_t shape {tuple(k_t.shape)} does not cover (batch {B}, Hkv {shape.num_kv_heads}, "
+                         f"d {d}, max_seq_len {shape.max_seq_len})")
+    if not isinstance(feature_counts, torch.Tensor) or feature_counts.dtype != torch.uint8 or \
+            tuple(feature_counts.shape) != (B, shape.num_kv_heads, d) or not feature_counts.is_contiguous() or \
+            feature_counts.device != q.device:
+        raise ValueError(f"feature_counts must be a contiguous uint8 [{B}, {shape.num_kv_heads}, {d}] tensor")
+    st = k_t.stride()
+    kt = KtLayout(st[0], st[1], st[2])
+    _check(library().santa_decode_bernoulli(ctypes.byref(shape), _ptr(q), _ptr(k_t), ctypes.byref(kt),
+                                            _ptr(v_cache), _ptr(seq_lens), int(num_samples), int(mode),
+                                            ctypes.c_uint64(seed & (2 ** 64 - 1)), int(num_bernoulli), _ptr(o),
+                                            _ptr(idx), _ptr(feature_counts), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "santa_decode_bernoulli")
 
 
 def santa_noalloc_scratch_bytes() -> int:

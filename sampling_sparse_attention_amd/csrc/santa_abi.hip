@@ -207,6 +207,10 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->items = (int32_t)((int64_t)s->batch * s->num_kv_heads * plan->T);
     p->item_order = santa::kOrderSplitFastest;
     p->use_ticket = 0;
+    p->kt = nullptr;
+    p->kt_stride_seq = p->kt_stride_head = p->kt_stride_feat = 0;
+    p->bern_B = 0;
+    p->bern_counts = nullptr;
     p->S = S;
     p->mode = mode;
     return SANTA_STATUS_OK;
@@ -222,12 +226,12 @@ santa_status hip_check(hipError_t e, const char* what) {
 // order), when one group's splits fit on a single compute die (XCD); 2 =
 // score pass + sample pass; 0 = unknown (HIP error).  The fused kernel's
 // workgroups wait for the other splits of their group.
-int choose_path(const santa::Params& p, int dtype) {
+int choose_path(const santa::Params& p, int dtype, bool bernoulli = false) {
     int dev = 0, cus = 0, xccs = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xccs < 1) xccs = 1;
-    const int per_cu = santa::fused_blocks_per_cu(p, dtype);
+    const int per_cu = bernoulli ? santa::bern_fused_blocks_per_cu(p, dtype) : santa::fused_blocks_per_cu(p, dtype);
     if (per_cu <= 0) return 0;
     if ((int64_t)per_cu * cus >= (int64_t)p.items) return 1;
     return (int64_t)per_cu * (cus / xccs) >= (int64_t)p.T ? 3 : 2;
@@ -487,6 +491,60 @@ santa_status santa_decode_topk(const santa_shape* shape, const void* q, const vo
     st = hip_check(santa::launch_score(p, shape->dtype, hs, false), "launching the score pass");
     if (st != SANTA_STATUS_OK) return st;
     st = hip_check(santa::launch_topk(p, shape->dtype, hs), "launching the top-k selection");
+    if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_decode_bernoulli(const santa_shape* shape, const void* q, const void* k_t,
+                                    const santa_kt_layout* kt, const void* v_cache, const int32_t* seq_lens,
+                                    int32_t num_samples, int32_t mode, uint64_t seed, int32_t num_bernoulli,
+                                    float* o, int32_t* idx, uint8_t* feature_counts, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    santa::Params p;
+    Plan plan;
+    santa_status st = make_params(shape, q, k_t, v_cache, seq_lens, nullptr, num_samples, mode, seed, o, idx,
+                                  workspace, workspace_bytes, &p, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    if (!kt || !feature_counts) return fail(SANTA_STATUS_INVALID_ARGUMENT, "kt layout or feature_counts is NULL");
+    if (shape->page_size != 0)
+        return fail(SANTA_STATUS_UNSUPPORTED, "santa_decode_bernoulli reads a contiguous K^T (page_size must be 0)");
+    if (num_bernoulli < 1 || num_bernoulli > santa::kMaxBernoulli)
+        return fail(SANTA_STATUS_UNSUPPORTED, "num_bernoulli %d not in [1, %d]", num_bernoulli, santa::kMaxBernoulli);
+    const int64_t eb = plan.elem_bytes;
+    if (kt->stride_feat < shape->max_seq_len || kt->stride_seq < 0 || kt->stride_head < 0)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "K^T rows must hold max_seq_len tokens (stride_feat %lld < %d)",
+                    (long long)kt->stride_feat, shape->max_seq_len);
+    if ((kt->stride_feat * eb) % 16 || (kt->stride_seq * eb) % 16 || (kt->stride_head * eb) % 16)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "K^T strides must keep every row 16-byte aligned");
+    p.kt = k_t;
+    p.kt_stride_seq = kt->stride_seq;
+    p.kt_stride_head = kt->stride_head;
+    p.kt_stride_feat = kt->stride_feat;
+    p.bern_B = num_bernoulli;
+    p.bern_counts = feature_counts;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int path = choose_path(p, shape->dtype, true);
+    if (path == 0) return fail(SANTA_STATUS_HIP_ERROR, "querying the device for the launch plan failed");
+    if (mode == SANTA_MODE_MULTINOMIAL) {
+        st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
+        if (st != SANTA_STATUS_OK) return st;
+    }
+    st = hip_check(santa::launch_bern_counts(p, shape->dtype, hs), "launching the feature counts");
+    if (st != SANTA_STATUS_OK) return st;
+    if (path == 1 || path == 3) {
+        if (path == 1) {
+            p.item_order = p.T % 8 == 0 ? santa::kOrderTokenBlocks : santa::kOrderHeadFastest;
+        } else {
+            p.item_order = santa::kOrderSplitFastest;
+            p.use_ticket = 1;
+        }
+        st = hip_check(santa::launch_bern_fused(p, shape->dtype, hs), "launching the fused Bernoulli kernel");
+    } else {
+        st = hip_check(santa::launch_bern_score(p, shape->dtype, hs), "launching the Bernoulli score pass");
+        if (st == SANTA_STATUS_OK)
+            st = hip_check(santa::launch_sample(p, shape->dtype, hs), "launching the sample pass");
+    }
     if (st != SANTA_STATUS_OK) return st;
     g_error[0] = '\0';
     return SANTA_STATUS_OK;

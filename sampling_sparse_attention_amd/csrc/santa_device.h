@@ -251,6 +251,10 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct Bf16 {
     static constexpr int bytes = 2;
+    // element i of a bf16 array, widened exactly
+    __device__ static __forceinline__ float elem(const void* base, int64_t i) {
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
+    }
     // dot product of 8 bf16 of a key row with 8 bf16 of a query (16 bytes each)
     __device__ static __forceinline__ float dot16(const uint4& k, const uint4& q, float acc) {
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
@@ -277,6 +281,9 @@ struct Bf16 {
 
 struct F32 {
     static constexpr int bytes = 4;
+    __device__ static __forceinline__ float elem(const void* base, int64_t i) {
+        return reinterpret_cast<const float*>(base)[i];
+    }
     __device__ static __forceinline__ float dot16(const uint4& k, const uint4& q, float acc) {
         acc = fmaf(__uint_as_float(k.x), __uint_as_float(q.x), acc);
         acc = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), acc);

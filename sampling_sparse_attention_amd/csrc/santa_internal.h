@@ -87,6 +87,14 @@ struct Params {
     int32_t use_ticket;           // fused kernel: items taken in start order from sync->ticket
     int32_t S;
     int32_t mode;
+    // Bernoulli qK^T: K transposed ([B, Hkv, d, tokens], tokens contiguous), the
+    // number of Bernoulli draws, and the feature counts [B, Hkv, d]
+    const void* kt;
+    int64_t kt_stride_seq;
+    int64_t kt_stride_head;
+    int64_t kt_stride_feat;
+    int32_t bern_B;
+    uint8_t* bern_counts;
 };
 
 // Dynamic LDS bytes of the split kernels for a group size, head dim, split and
@@ -101,6 +109,13 @@ hipError_t launch_targets(const Params& p, hipStream_t stream);
 // stats = false: scores to the stash only (no split statistics or records)
 hipError_t launch_score(const Params& p, int dtype, hipStream_t stream, bool stats = true);
 hipError_t launch_topk(const Params& p, int dtype, hipStream_t stream);
+// Bernoulli qK^T: the feature counts, then the fused kernel (grid p.items, items
+// by ticket when p.use_ticket) or the score pass of the two-kernel path
+hipError_t launch_bern_counts(const Params& p, int dtype, hipStream_t stream);
+hipError_t launch_bern_fused(const Params& p, int dtype, hipStream_t stream);
+hipError_t launch_bern_score(const Params& p, int dtype, hipStream_t stream);
+int bern_fused_blocks_per_cu(const Params& p, int dtype);
+constexpr int kMaxBernoulli = 64;        // Bernoulli draws per feature
 constexpr int kMaxTopk = 8192;           // largest k of the top-k comparator
 hipError_t launch_sample(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_fused(const Params& p, int dtype, hipStream_t stream);

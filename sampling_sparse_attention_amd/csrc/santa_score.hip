@@ -36,20 +36,7 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
             split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
             __syncthreads();
         }
-        // the stash: scaled scores of the split, coalesced 16-byte stores
-        constexpr int NW = NT / 64;
-        const int lane = threadIdx.x & 63;
-        for (int h = threadIdx.x >> 6; h < G; h += NW) {
-            const float* row = sc + h * p.split;
-            float* dst = p.stash + ((int64_t)it.b * p.Hq + it.g * G + h) * p.stash_row + it.key0;
-            for (int i = lane * 4; i < it.ns; i += 256) {
-                if (i + 4 <= it.ns) {
-                    *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(row + i);
-                } else {
-                    for (int e = i; e < it.ns; ++e) dst[e] = row[e];
-                }
-            }
-        }
+        write_stash<G, NT>(p, it, sc);
     }
 }
 

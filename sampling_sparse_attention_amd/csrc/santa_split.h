@@ -1178,4 +1178,117 @@ __device__ __forceinline__ void write_empty(const Params& p, const Item& it) {
     for (int i = threadIdx.x; i < G * p.S; i += NT) idx[i] = -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// The score stash of the two-kernel path: the split's scaled scores from LDS
+// (sc[h * split + local]) to stash row (b, g * G + h) at the split's first key,
+// with coalesced 16-byte stores.
+// ---------------------------------------------------------------------------
+template <int G, int NT>
+__device__ __forceinline__ void write_stash(const Params& p, const Item& it, const float* sc) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    for (int h = threadIdx.x >> 6; h < G; h += NW) {
+        const float* row = sc + h * p.split;
+        float* dst = p.stash + ((int64_t)it.b * p.Hq + it.g * G + h) * p.stash_row + it.key0;
+        for (int i = lane * 4; i < it.ns; i += 256) {
+            if (i + 4 <= it.ns) {
+                *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(row + i);
+            } else {
+                for (int e = i; e < it.ns; ++e) dst[e] = row[e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The work item of a fused-kernel workgroup, -1 if it has none.  A workgroup
+// waits only for the statistics of the other splits of its (sequence, KV
+// head) group; two ways to guarantee that every statistic a workgroup waits
+// for is computed by a workgroup that runs:
+//   - the device holds every workgroup of the grid at once (blockIdx gives
+//     the item);
+//   - tickets: each workgroup takes the next item from an atomic counter when
+//     it starts, items numbered group by group, and one group's splits fit on
+//     any single compute die (XCD).  A workgroup waits only for items of its
+//     own group.  Once a ticket of the next group is taken, every ticket of
+//     this group has been, so a workgroup that cannot be placed is kept out
+//     only by workgroups of earlier groups, which finish without waiting for
+//     later ones, or of this group.  A die whose slots all hold waiting
+//     workgroups of one group would hold the whole group, so while tickets of
+//     a group remain untaken some die that still has workgroups to start has
+//     a slot that frees.  (Room for one group on the whole device is not
+//     enough: the die a workgroup runs on is fixed by its index, and when
+//     some dies run out of workgroups the remaining tickets can only be
+//     taken on dies that one group's waiting workgroups may fill.)  The
+//     groups' K streams and latency-bound tails then overlap from one group
+//     to the next.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int take_item(const Params& p) {
+    if (!p.use_ticket) return blockIdx.x;
+    __shared__ int s_item;
+    if (threadIdx.x == 0) {
+        const unsigned int k = __hip_atomic_fetch_add(&p.sync->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the last ticket of the launch: every other one has been taken, so the
+        // counter returns to zero for the next call
+        if (k == (unsigned int)p.items - 1u)
+            __hip_atomic_store(&p.sync->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // a counter that did not start at zero (a workspace never cleared): no
+        // item, and the call is marked failed
+        if (k >= (unsigned int)p.items)
+            __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_item = k < (unsigned int)p.items ? (int)k : -1;
+    }
+    __syncthreads();
+    return s_item;
+}
+
+// ---------------------------------------------------------------------------
+// One work item of the fused decode kernel: the whole step of section 3.2 of
+// "Stochastic Sparse Attention for Memory-Bound Inference" (score pass, global
+// budget, parallel gather) for one (sequence, KV head, split), with the
+// split's scores kept in LDS across the wait for the other splits.
+// stream(it, sc, pages) fills the scaled scores sc[h * split + local] of the
+// item's keys for the G heads (the exact scores of Eq. 1, or an estimate of
+// them); err0 is the workspace's error word as read at the start.
+// ---------------------------------------------------------------------------
+template <int G, int D, typename E, int NT, typename Stream>
+__device__ __forceinline__ void fused_item(const Params& p, const Item& it, unsigned int err0, unsigned char* smem,
+                                           Stream&& stream) {
+    if (it.n == 0) {
+        if (it.t == 0) write_empty<G, D, NT>(p, it);
+        return;
+    }
+    if (it.ns == 0) return;
+    const LdsLayout L = lds_layout(G, D, p.split, NT);
+    float* sc = reinterpret_cast<float*>(smem + L.scratch);
+    int* pages = reinterpret_cast<int*>(smem + L.pages);
+    HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
+
+    __shared__ int s_fail;              // a wait of this workgroup gave up
+    if (threadIdx.x == 0) s_fail = 0;
+    load_pages<NT>(p, it, pages);
+    __syncthreads();
+    stream(it, sc, pages);
+    __shared__ unsigned int s_err;      // thread 0's read, the same for the whole workgroup
+    if (threadIdx.x == 0) s_err = err0;
+    __syncthreads();
+    // an earlier call left the workspace in error: its counts and records are
+    // stale, so nothing of this call can be trusted
+    if (s_err) {
+        if (it.t == 0) poison_group<G, D, NT>(p, it);
+        return;
+    }
+    // each head's wave publishes its record; a reader re-reads a record until it
+    // is written, so neither a workgroup barrier nor the stores' completion is
+    // needed before the count at the group barrier
+    split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
+    if (!group_barrier(p, it, [&] { systematic_offsets<G, 1>(p, it, hs); })) {
+        poison_group<G, D, NT>(p, it);      // the barrier's result is the same in every thread
+        return;
+    }
+    prefix_and_sample<G, D, E, NT>(p, it, L, smem, kSpinLimit, &s_fail);
+    finish_output<G, D, NT>(p, it, &s_fail);
+}
+
 }  // namespace santa

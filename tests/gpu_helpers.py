@@ -92,14 +92,16 @@ class ParityReport:
                 f"boundary_mismatches={self.boundary_mismatch} worst_rel_l2={self.worst_rel_l2:.2e}")
 
 
-def check_head(rep: ParityReport, ref: dict, idx_gpu: np.ndarray, o_gpu: np.ndarray, where: str):
-    """idx exact outside the boundary window; o within O_REL_L2 of the fp64 gather of idx_gpu."""
+def check_head(rep: ParityReport, ref: dict, idx_gpu: np.ndarray, o_gpu: np.ndarray, where: str,
+               window: float = BOUNDARY_WINDOW):
+    """idx exact outside the boundary window (``window`` in CDF units); o within
+    O_REL_L2 of the fp64 gather of idx_gpu."""
     t, F, delta = ref["t"], ref["F"], ref["delta"]
     n = len(ref["p"])
     rep.heads += 1
     rep.targets += len(t)
     assert idx_gpu.min() >= 0 and idx_gpu.max() < n, f"{where}: index out of range"
-    near = delta < BOUNDARY_WINDOW
+    near = delta < window
     rep.boundary += int(near.sum())
     bad = idx_gpu != ref["idx"]
     far_bad = bad & ~near
@@ -109,7 +111,7 @@ def check_head(rep: ParityReport, ref: dict, idx_gpu: np.ndarray, o_gpu: np.ndar
     if bad.any():
         gi = idx_gpu[bad]
         tb = t[bad]
-        ok = (F[gi] - BOUNDARY_WINDOW <= tb) & (tb < F[gi + 1] + BOUNDARY_WINDOW)
+        ok = (F[gi] - window <= tb) & (tb < F[gi + 1] + window)
         assert ok.all(), f"{where}: a boundary-case index is not adjacent to its target"
         rep.boundary_mismatch += int(bad.sum())
     own = O.estimate(ref["v"], idx_gpu)

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert len(declared) == 18
+    assert len(declared) == 19
     out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (santa_\w+)", out))
@@ -246,6 +246,30 @@ def test_decode_args_validates_before_launch(lib):
     need0 = santa.santa_workspace_size(shape, 64, 0)
     assert call(algorithm=1, mode=0, workspace_bytes=need0) == UNSUPPORTED   # flash: stratified/systematic
     assert call(flags=1, num_samples=0) == INVALID
+
+
+def test_bernoulli_validates_before_touching_the_device(lib):
+    """santa_decode_bernoulli checks its K^T layout, B and the cache kind on the host."""
+    shape = _shape(max_seq_len=1024, kv_stride_seq=1024 * 8 * 128)
+    need = santa.santa_workspace_size(shape, 64, 2)
+    fake = ctypes.c_void_p(1 << 20)
+    good = santa.KtLayout(8 * 128 * 1024, 128 * 1024, 1024)
+
+    def call(kt=good, B=8, counts=fake, shp=shape, k_t=fake):
+        return lib.santa_decode_bernoulli(ctypes.byref(shp), fake, k_t, None if kt is None else ctypes.byref(kt),
+                                          fake, fake, 64, 2, ctypes.c_uint64(0), B, fake, fake, counts, fake,
+                                          need, None)
+
+    assert call(kt=None) == INVALID
+    assert call(counts=None) == INVALID
+    assert call(k_t=ctypes.c_void_p((1 << 20) + 8)) == INVALID          # K^T not 16-byte aligned
+    assert call(B=0) == UNSUPPORTED and call(B=65) == UNSUPPORTED
+    assert "num_bernoulli" in lib.santa_last_error().decode()
+    assert call(kt=santa.KtLayout(8 * 128 * 1024, 128 * 1024, 1000)) == INVALID     # rows shorter than n_max
+    assert call(kt=santa.KtLayout(8 * 128 * 1028, 128 * 1028, 1028)) == INVALID     # rows not 16-byte aligned
+    paged = _shape(max_seq_len=1024, page_size=16, pages_per_seq=64, num_pages=64)
+    assert lib.santa_decode_bernoulli(ctypes.byref(paged), fake, fake, ctypes.byref(good), fake, fake, 64, 2,
+                                      ctypes.c_uint64(0), 8, fake, fake, fake, fake, need, None) == INVALID
 
 
 def test_workspace_status_validates_before_touching_the_device(lib):
