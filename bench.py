@@ -16,8 +16,10 @@ gives the median of the per-round times with a 95 % bootstrap interval.
 The JSON line also carries: the roofline of the dominant kernel (the fused
 decode kernel, bound by HBM bandwidth: all of K plus the distinct sampled V rows
 per launch), the HBM bandwidth of a plain device copy measured in the same run,
-the two-kernel path and S^2ANTA-flash on the same inputs, the Qwen2.5-7B-shaped
-long-context step (all three sampling rules), a parity sample of the timed
+the two-kernel path, S^2ANTA-flash and the top-k comparator on the same inputs,
+the Qwen2.5-7B-shaped long-context step (all three sampling rules), Bernoulli
+qK^T (B = 8 draws, with the fraction of key features read) beside the exact step
+on the same inputs, a parity sample of the timed
 configuration against the oracle (boundary cases, largest CDF difference), and
 the CPU oracle timed on a bounded sample of the same workload.
 """
@@ -376,6 +378,53 @@ def qwen_line(santa, steps, eager, dev):
     return out
 
 
+def bern_line(santa, steps, eager, dev, ncopies):
+    """Bernoulli qK^T with the mean group query (B = 8 draws) on the Llama-shaped step
+    with log-normal query channel scales, beside the exact step on the same inputs.
+    Algorithmic bytes: the kept feature rows of K^T (count > 0) plus the distinct
+    sampled V rows."""
+    w = W.WORKLOADS["bern32k"]
+    S, mode, B = w.samples[0], w.modes[0], w.bernoulli
+    copies = make_copies(w, ncopies, dev)
+    for x in copies:
+        x["kt"] = W.keys_transposed(x)
+    run = Runner(santa, copies, S, mode, 0)
+    counts = torch.empty((w.batch, w.kv_heads, w.head_dim), dtype=torch.uint8, device=dev)
+
+    def bern(c):
+        x = copies[c % len(copies)]
+        santa.santa_decode_bernoulli(run.shape, x["q"], x["kt"], x["v"], x["seq_lens"], S, mode, run.seed, B,
+                                     run.o, run.idx, counts, run.ws)
+
+    for i in range(20):
+        bern(i)
+    t_b, r_b, c_b = timed(bern, steps, eager, ncopies)
+    t_e, r_e, c_e = timed(run.step, steps, eager, ncopies)
+    lens = copies[0]["seq_lens"].cpu().tolist()
+    k_read, feats, uniq = [], [], []
+    for c in range(ncopies):
+        bern(c)
+        torch.cuda.synchronize()
+        cnt = counts.cpu()
+        kept = (cnt > 0).sum(dim=2)                       # [B, Hkv]
+        k_read.append(sum(int(kept[b].sum()) * int(lens[b]) for b in range(w.batch)) * w.elem_bytes)
+        feats.append(float((cnt > 0).double().mean()))
+        uniq.append(W.unique_v_rows(run.idx.cpu(), w.group))
+    kb = sum(k_read) / ncopies
+    u = sum(uniq) / ncopies
+    alg = kb + u * w.head_dim * w.elem_bytes
+    out = {"config": {"batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads, "head_dim": w.head_dim,
+                      "seq_len": w.seq_len, "samples": S, "mode": W.MODE_NAMES[mode], "draws": B,
+                      "q_channel_sigma": w.q_channel_sigma, "kv_copies": ncopies},
+           "step_us": t_b * 1e6, "calls_timed": c_b, "rounds": round_stats(r_b),
+           "key_feature_access": sum(feats) / ncopies, "k_bytes_read": kb, "unique_v_rows": u,
+           "algorithmic_bytes": alg, "achieved_GBs": alg / t_b / 1e9, "frac_of_peak": alg / t_b / 1e9 / PEAK_HBM_GBS,
+           "exact_step_us": t_e * 1e6, "exact_rounds": round_stats(r_e)}
+    del run, copies
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -490,10 +539,11 @@ def main(argv=None):
         rec["roofline"]["frac_of_measured_copy"] = achieved / c
         rec["step"]["dense_read_us_at_measured_copy"] = dense / (c * 1e9) * 1e6
     if not args.no_extras and args.workload == "llama32k":
-        print("[bench] timing the Qwen-shaped step", file=sys.stderr, flush=True)
+        print("[bench] timing the Qwen-shaped step and Bernoulli qK^T", file=sys.stderr, flush=True)
         del copies, run
         torch.cuda.empty_cache()
         rec["qwen128k"] = qwen_line(santa, min(args.steps, 400), args.eager, dev)
+        rec["bernoulli"] = bern_line(santa, min(args.steps, 400), args.eager, dev, ncopies)
         copies = make_copies(w, 1, dev)
         run = Runner(santa, copies, S, mode, args.split)
     if not args.no_cpu_baseline:

@@ -334,6 +334,11 @@ typedef struct santa_kt_layout {
  * santa_decode does (same num_samples, mode and seed conventions).  Only the
  * features with count_i > 0 are read from K^T, so skipped features cost no
  * bytes; feature_counts [B, Hkv, d] (uint8, device) receives count_i.
+ * Arithmetic of s_hat: the weights (max m / B) count_i / m_i q_{h,i} are
+ * formed in fp64 and rounded once to fp32; the kept features, ascending, are
+ * dealt round-robin to F lane groups (F a power of two, 1 <= F <= 32, set by
+ * the split size and dtype), each group sums its terms by fp32 fused
+ * multiply-adds in that order, and the F group sums are added pairwise.
  *
  *   shape        sizes and the layout of v_cache (contiguous: page_size 0)
  *   k_t, kt      K transposed and its layout (santa_kt_layout)

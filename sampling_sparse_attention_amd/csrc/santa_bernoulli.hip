@@ -54,23 +54,41 @@ __device__ __forceinline__ double mean_abs_query(const Params& p, int b, int g, 
     return m / (double)G;
 }
 
+// One workgroup per (sequence, KV head) group, one thread per (feature,
+// slice of draws): thread t takes feature t mod 128 and the draws
+// n = t / 128, t / 128 + 8, ...; the slices' counts are summed in LDS.
+constexpr int kCountThreads = 1024;
+constexpr int kCountSlices = kCountThreads / 128;
+
 template <int G, typename E>
-__global__ __launch_bounds__(128) void bern_counts_kernel(Params p) {
-    __shared__ double s_max[2];
+__global__ __launch_bounds__(kCountThreads) void bern_counts_kernel(Params p) {
+    __shared__ double s_m[128];
+    __shared__ double s_max[kCountThreads / 64];
+    __shared__ int s_cnt[kCountSlices][128];
     const int grp = blockIdx.x;
     const int b = grp / p.Hkv, g = grp - b * p.Hkv;
-    const int i = threadIdx.x;
-    float qv[G];
-    const double m = i < p.D ? mean_abs_query<G, E>(p, b, g, i, qv) : 0.0;
-    const double top = block_max_f64(m, 2, s_max);
-    if (i >= p.D) return;
+    const int i = threadIdx.x & 127, slice = threadIdx.x >> 7;
+    double m = 0.0;
+    if (slice == 0 && i < p.D) {
+        float qv[G];
+        m = mean_abs_query<G, E>(p, b, g, i, qv);
+        s_m[i] = m;
+    }
+    const double top = block_max_f64(m, kCountThreads / 64, s_max);     // its barriers publish s_m
     int count = 0;
-    if (top > 0.0) {
-        const double pi = m / top;
-        for (int n = 0; n < p.bern_B; ++n)
+    if (i < p.D && top > 0.0) {
+        const double pi = s_m[i] / top;
+        for (int n = slice; n < p.bern_B; n += kCountSlices)
             if (((double)n + bern_uniform(p.seed, b, g, i, n)) / (double)p.bern_B < pi) ++count;
     }
-    p.bern_counts[(int64_t)grp * p.D + i] = (uint8_t)count;
+    s_cnt[slice][i] = count;
+    __syncthreads();
+    if (slice == 0 && i < p.D) {
+        int c = 0;
+#pragma unroll
+        for (int k = 0; k < kCountSlices; ++k) c += s_cnt[k][i];
+        p.bern_counts[(int64_t)grp * p.D + i] = (uint8_t)c;
+    }
 }
 
 // The group's kept features and, per head, their weights m_hat_i / m_i * q_{h,i}.
@@ -111,80 +129,88 @@ __device__ __forceinline__ void bern_prologue(const Params& p, const Item& it, B
     __syncthreads();
 }
 
-// Estimated scores of the split's keys: wave w takes keys [w * split / NW,
-// (w + 1) * split / NW), lane l KPL consecutive ones of them, and sums over
-// the kept features weight * K^T[feature][key] for the G heads; every load
-// reads KPL contiguous token values of one feature.
-template <int G, typename E, int NT, int KPL>
+// Estimated scores of the split's keys.  Every lane reads one 16-byte piece
+// of a feature row per kept feature it takes: wave w covers the keys
+// [w * split / NW, (w + 1) * split / NW), lane l the KPL keys from
+// (l mod L) * KPL on (L lanes per row piece), and the 64 / L lane groups of a
+// wave deal the kept features out round-robin (group r takes the r-th, the
+// (r + 64/L)-th, ... in ascending feature order).  Each lane sums its features
+// with fused multiply-adds in that order; the groups' sums are then added
+// pairwise (xor butterfly, the same result in every lane of a key).
+template <int G, typename E, int NT>
 __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, float* sc, const BernFeatures<G>& bf) {
     constexpr int NW = NT / 64;
-    constexpr int UF = 8;                      // features whose loads are in flight at once
+    constexpr int KPL = 16 / E::bytes;         // keys per lane: one 16-byte load per feature row
+    constexpr int UF = G * KPL >= 32 ? 4 : 8;  // features a lane has in flight at once (registers)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lk = wave * (p.split / NW) + lane * KPL;      // first local key of this lane
-    const bool active = lane * KPL < p.split / NW && lk < it.ns;
-    const bool full = active && lk + KPL <= it.ns;
+    const int per_wave = p.split / NW;         // 16 .. 256 keys
+    const int L = per_wave / KPL;              // lanes per row piece: 2 .. 64
+    const int nfg = 64 / L;                    // feature groups of the wave
+    const int fg = lane / L;
+    const int lk = wave * per_wave + (lane - fg * L) * KPL;      // first local key of this lane
+    const bool active = lk < it.ns;
+    const bool full = lk + KPL <= it.ns;
     const char* base = reinterpret_cast<const char*>(p.kt) +
                        ((int64_t)it.b * p.kt_stride_seq + (int64_t)it.g * p.kt_stride_head + it.key0 +
                         (active ? lk : 0)) * E::bytes;
+    const int64_t row_bytes = p.kt_stride_feat * E::bytes;
     float acc[G][KPL];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int j = 0; j < KPL; ++j) acc[h][j] = 0.0f;
     const int nf = bf.n;
-    for (int f0 = 0; f0 < nf; f0 += UF) {
-        float x[UF][KPL];
+    for (int f0 = fg; f0 < nf; f0 += UF * nfg) {
+        uint4 raw[UF];
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
-            const int f = f0 + u;
-            const char* row = base + (int64_t)bf.feat[f < nf ? f : 0] * p.kt_stride_feat * E::bytes;
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) x[u][j] = 0.0f;
-            if (f < nf && full) {
-                if constexpr (E::bytes * KPL == 16) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(row);
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int j = 0; j < KPL; ++j) x[u][j] = __uint_as_float(w4[j]);
-                } else if constexpr (E::bytes * KPL == 8) {
-                    const uint2 v = *reinterpret_cast<const uint2*>(row);
-                    if constexpr (E::bytes == 2) {
-                        x[u][0] = __uint_as_float(v.x << 16);
-                        x[u][1] = __uint_as_float(v.x & 0xFFFF0000u);
-                        x[u][2] = __uint_as_float(v.y << 16);
-                        x[u][3] = __uint_as_float(v.y & 0xFFFF0000u);
-                    } else {
-                        x[u][0] = __uint_as_float(v.x);
-                        x[u][1] = __uint_as_float(v.y);
-                    }
-                } else if constexpr (E::bytes * KPL == 4) {
-                    const uint32_t v = *reinterpret_cast<const uint32_t*>(row);
-                    if constexpr (E::bytes == 2) {
-                        x[u][0] = __uint_as_float(v << 16);
-                        x[u][1] = __uint_as_float(v & 0xFFFF0000u);
-                    } else {
-                        x[u][0] = __uint_as_float(v);
-                    }
+            const int f = f0 + u * nfg;
+            raw[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (f < nf && active) {
+                const char* row = base + (int64_t)bf.feat[f] * row_bytes;
+                if (full) {
+                    raw[u] = *reinterpret_cast<const uint4*>(row);
                 } else {
-                    x[u][0] = E::elem(row, 0);
+                    // the sequence ends inside this lane's keys: element by element
+                    uint32_t w4[4] = {0u, 0u, 0u, 0u};
+                    for (int j = 0; lk + j < it.ns; ++j) {
+                        const uint32_t bits = __float_as_uint(E::elem(row, j));
+                        if constexpr (E::bytes == 2)
+                            w4[j >> 1] |= (j & 1) ? (bits & 0xFFFF0000u) : (bits >> 16);
+                        else
+                            w4[j] = bits;
+                    }
+                    raw[u] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
                 }
-            } else if (f < nf && active) {
-                // the split's last keys: element by element up to the end of the sequence
-                for (int j = 0; j < KPL && lk + j < it.ns; ++j) x[u][j] = E::elem(row, j);
             }
         }
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
-            const int f = f0 + u < nf ? f0 + u : 0;
+            const int f = f0 + u * nfg;
+            const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+            float x[KPL];
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) {
+                if constexpr (E::bytes == 2)
+                    x[j] = __uint_as_float((j & 1) ? (w4[j >> 1] & 0xFFFF0000u) : (w4[j >> 1] << 16));
+                else
+                    x[j] = __uint_as_float(w4[j]);
+            }
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float wt = f0 + u < nf ? bf.w[h][f] : 0.0f;
+                const float wt = f < nf ? bf.w[h][f] : 0.0f;
 #pragma unroll
-                for (int j = 0; j < KPL; ++j) acc[h][j] = fmaf(wt, x[u][j], acc[h][j]);
+                for (int j = 0; j < KPL; ++j) acc[h][j] = fmaf(wt, x[j], acc[h][j]);
             }
         }
     }
-    if (active) {
+    for (int off = L; off < 64; off <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < KPL; ++j) acc[h][j] += __shfl_xor(acc[h][j], off, 64);
+    }
+    if (fg == 0 && active) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -194,14 +220,14 @@ __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, flo
     priority_tail();
 }
 
-template <int G, typename E, int NT, int KPL>
+template <int G, typename E, int NT>
 __device__ __forceinline__ void bern_scores(const Params& p, const Item& it, float* sc) {
     __shared__ BernFeatures<G> bf;
     bern_prologue<G, E, NT>(p, it, bf);
-    bern_stream<G, E, NT, KPL>(p, it, sc, bf);
+    bern_stream<G, E, NT>(p, it, sc, bf);
 }
 
-template <int G, int D, typename E, int NT, int KPL>
+template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
 void bern_fused_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -210,10 +236,10 @@ void bern_fused_kernel(Params p) {
     priority_streaming();
     const unsigned int err0 = p.sync->error;
     fused_item<G, D, E, NT>(p, make_item(p, item), err0, smem,
-                            [&](const Item& it, float* sc, const int*) { bern_scores<G, E, NT, KPL>(p, it, sc); });
+                            [&](const Item& it, float* sc, const int*) { bern_scores<G, E, NT>(p, it, sc); });
 }
 
-template <int G, int D, typename E, int NT, int KPL>
+template <int G, int D, typename E, int NT>
 __global__ __launch_bounds__(NT) void bern_score_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
     const Item it = make_item(p, blockIdx.x);
@@ -221,46 +247,34 @@ __global__ __launch_bounds__(NT) void bern_score_kernel(Params p) {
     const LdsLayout L = lds_layout(G, D, p.split, NT);
     float* sc = reinterpret_cast<float*>(smem + L.scratch);
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
-    bern_scores<G, E, NT, KPL>(p, it, sc);
+    bern_scores<G, E, NT>(p, it, sc);
     __syncthreads();
     split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     __syncthreads();
     write_stash<G, NT>(p, it, sc);
 }
 
-// Keys per lane: a wave covers split / 4 keys, at most four per lane.
-inline int bern_kpl(int split) {
-    const int per_lane = split / (kThreads / 64) / 64;
-    return per_lane >= 4 ? 4 : per_lane >= 2 ? 2 : 1;
-}
-
-template <int G, int D, typename E, int KPL>
-static const void* bern_fn(bool fused) {
-    return fused ? reinterpret_cast<const void*>(&bern_fused_kernel<G, D, E, kThreads, KPL>)
-                 : reinterpret_cast<const void*>(&bern_score_kernel<G, D, E, kThreads, KPL>);
-}
-
 template <int G, int D, typename E>
-static const void* bern_fn_k(int kpl, bool fused) {
-    return kpl == 4 ? bern_fn<G, D, E, 4>(fused) : kpl == 2 ? bern_fn<G, D, E, 2>(fused) : bern_fn<G, D, E, 1>(fused);
+static const void* bern_fn(bool fused) {
+    return fused ? reinterpret_cast<const void*>(&bern_fused_kernel<G, D, E, kThreads>)
+                 : reinterpret_cast<const void*>(&bern_score_kernel<G, D, E, kThreads>);
 }
 
 template <int D, typename E>
-static const void* bern_fn_g(int G, int kpl, bool fused) {
+static const void* bern_fn_g(int G, bool fused) {
     switch (G) {
-        case 1: return bern_fn_k<1, D, E>(kpl, fused);
-        case 2: return bern_fn_k<2, D, E>(kpl, fused);
-        case 4: return bern_fn_k<4, D, E>(kpl, fused);
-        case 7: return bern_fn_k<7, D, E>(kpl, fused);
-        case 8: return bern_fn_k<8, D, E>(kpl, fused);
+        case 1: return bern_fn<1, D, E>(fused);
+        case 2: return bern_fn<2, D, E>(fused);
+        case 4: return bern_fn<4, D, E>(fused);
+        case 7: return bern_fn<7, D, E>(fused);
+        case 8: return bern_fn<8, D, E>(fused);
         default: return nullptr;
     }
 }
 
 static const void* bern_function(const Params& p, int dtype, bool fused) {
-    const int kpl = bern_kpl(p.split);
-    if (dtype == 0) return p.D == 64 ? bern_fn_g<64, Bf16>(p.G, kpl, fused) : bern_fn_g<128, Bf16>(p.G, kpl, fused);
-    return p.D == 64 ? bern_fn_g<64, F32>(p.G, kpl, fused) : bern_fn_g<128, F32>(p.G, kpl, fused);
+    if (dtype == 0) return p.D == 64 ? bern_fn_g<64, Bf16>(p.G, fused) : bern_fn_g<128, Bf16>(p.G, fused);
+    return p.D == 64 ? bern_fn_g<64, F32>(p.G, fused) : bern_fn_g<128, F32>(p.G, fused);
 }
 
 static hipError_t launch_bern(const Params& p, int dtype, hipStream_t stream, bool fused) {
@@ -288,7 +302,7 @@ int bern_fused_blocks_per_cu(const Params& p, int dtype) {
 
 template <int G, typename E>
 static hipError_t launch_counts_t(const Params& p, hipStream_t stream) {
-    hipLaunchKernelGGL((bern_counts_kernel<G, E>), dim3((unsigned)(p.B * p.Hkv)), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((bern_counts_kernel<G, E>), dim3((unsigned)(p.B * p.Hkv)), dim3(kCountThreads), 0, stream, p);
     return hipGetLastError();
 }
 

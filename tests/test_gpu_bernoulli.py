@@ -6,12 +6,17 @@ against oracle/bernoulli.py through the C ABI.
 * The sampled indices equal the oracle's, which samples from its fp64
   estimated scores, except for targets within a CDF window of an interval
   edge.  The window is 1e-6 (the exact path's) plus twice the p-weighted bound
-  on the GPU's fp32 score error: the weights are rounded once to fp32 and the
-  kept features are summed by fused multiply-adds in feature order, so the
-  error of key j's score is at most 2^-24 (sum over the kept features of the
-  partial sums' magnitudes plus of |w_f k_jf|), divided by sqrt(d), plus the
-  rounding of the 1/sqrt(d) scale; a CDF moves by at most twice the p-weighted
-  mean of the scores' errors.
+  on the GPU's fp32 score error.  The library states its summation: the
+  weights are rounded once to fp32, the kept features (ascending) are dealt
+  round-robin to F lane groups (F a power of two up to 32, fixed by the split
+  size), each group sums its terms by fused multiply-adds and the F group sums
+  are added pairwise.  To first order the error of key j's score is then at
+  most 2^-24 times (the sum of |w_f k_jf| for the weights' rounding, plus the
+  magnitudes of every group's running sums, plus log2(F) times the sum of
+  |w_f k_jf| for the pairwise additions); the test takes the largest of these
+  over every F, divides by sqrt(d) and adds the rounding of the 1/sqrt(d)
+  scale.  A CDF moves by at most twice the p-weighted mean of the scores'
+  errors.
 * o lies within 1e-3 relative L2 of the fp64 gather-mean of the GPU's own
   indices.
 
@@ -80,8 +85,13 @@ def score_window(q_group, k, counts, B, h, s):
     ratio = np.divide((top / B) * counts, m, out=np.zeros_like(m), where=m > 0)
     feats = np.nonzero(counts)[0]
     terms = k[:, feats] * (q_group[h] * ratio)[feats]
-    part = np.cumsum(terms, axis=1)
-    e = 2.0 ** -24 * (np.abs(part).sum(1) + np.abs(terms).sum(1)) / math.sqrt(d) + 2.0 ** -23 * np.abs(s)
+    mag = np.abs(terms).sum(1)
+    worst = np.zeros(len(k))
+    for lg in range(6):                      # F = 1, 2, 4, ..., 32 lane groups
+        F = 1 << lg
+        run = sum(np.abs(np.cumsum(terms[:, r::F], axis=1)).sum(1) for r in range(F))
+        worst = np.maximum(worst, run + lg * mag)
+    e = 2.0 ** -24 * (worst + mag) / math.sqrt(d) + 2.0 ** -23 * np.abs(s)
     p = np.exp(s - s.max())
     p /= p.sum()
     return H.BOUNDARY_WINDOW + 2.0 * float((p * e).sum())
