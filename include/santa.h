@@ -314,6 +314,8 @@ santa_status santa_decode_topk(const santa_shape* shape, const void* q, const vo
  * (sequence b, KV head g, feature i, token j) at
  *   b * stride_seq + g * stride_head + i * stride_feat + j
  * (tokens contiguous; every row 16-byte aligned; stride_feat >= max_seq_len).
+ * Elements of a row past its sequence's length, below stride_feat, may be
+ * read and do not affect the result.
  */
 typedef struct santa_kt_layout {
     int64_t stride_seq;
@@ -335,18 +337,17 @@ typedef struct santa_kt_layout {
  * features with count_i > 0 are read from K^T, so skipped features cost no
  * bytes; feature_counts [B, Hkv, d] (uint8, device) receives count_i.
  * Arithmetic of s_hat: the weights (max m / B) count_i / m_i q_{h,i} are
- * formed in fp64 and rounded once to fp32; the kept features, ascending, are
- * dealt round-robin to F lane groups (F a power of two, 1 <= F <= 32, set by
- * the split size and dtype), each group sums its terms by fp32 fused
- * multiply-adds in that order, and the F group sums are added pairwise.
+ * formed in fp64 and rounded once to fp32, and each score is the sum of its
+ * kept features' terms by fp32 fused multiply-adds in ascending feature
+ * order, then multiplied by the fp32 1/sqrt(d).
  *
  *   shape        sizes and the layout of v_cache (contiguous: page_size 0)
  *   k_t, kt      K transposed and its layout (santa_kt_layout)
  *   v_cache      token-major V as in santa_decode
  *   num_bernoulli B, 1 <= B <= 64
  * Workspace: santa_workspace_size(shape, num_samples, mode) bytes.  Runs the
- * feature counts, then the fused kernel (or the score and sample passes)
- * chosen as for santa_decode.
+ * fused kernel (or the score and sample passes) chosen as for santa_decode;
+ * every workgroup derives its group's counts itself.
  */
 santa_status santa_decode_bernoulli(const santa_shape* shape, const void* q, const void* k_t,
                                     const santa_kt_layout* kt, const void* v_cache, const int32_t* seq_lens,

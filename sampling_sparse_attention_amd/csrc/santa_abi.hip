@@ -530,8 +530,6 @@ santa_status santa_decode_bernoulli(const santa_shape* shape, const void* q, con
         st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
         if (st != SANTA_STATUS_OK) return st;
     }
-    st = hip_check(santa::launch_bern_counts(p, shape->dtype, hs), "launching the feature counts");
-    if (st != SANTA_STATUS_OK) return st;
     if (path == 1 || path == 3) {
         if (path == 1) {
             p.item_order = p.T % 8 == 0 ? santa::kOrderTokenBlocks : santa::kOrderHeadFastest;

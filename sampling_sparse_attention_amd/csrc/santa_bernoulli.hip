@@ -11,11 +11,15 @@
 // skips its bytes.  The SANTA step that follows (statistics, global budget,
 // sampling, gather of token-major V rows) is the one of the exact path.
 //
-//   bern_counts_kernel   the feature counts of every (sequence, KV head),
-//                        written to the caller's [B, Hkv, d] array;
+// Every workgroup derives its group's feature counts itself (a few Philox
+// draws per feature, see bern_count); the first split of each group writes
+// them to the caller's [B, Hkv, d] array.
+//
 //   bern_fused_kernel    the fused decode kernel with the estimated scores;
 //   bern_score_kernel    the score pass of the two-kernel path (the sample
 //                        pass is the exact path's).
+#include <type_traits>
+
 #include "santa_split.h"
 
 namespace santa {
@@ -54,41 +58,30 @@ __device__ __forceinline__ double mean_abs_query(const Params& p, int b, int g, 
     return m / (double)G;
 }
 
-// One workgroup per (sequence, KV head) group, one thread per (feature,
-// slice of draws): thread t takes feature t mod 128 and the draws
-// n = t / 128, t / 128 + 8, ...; the slices' counts are summed in LDS.
-constexpr int kCountThreads = 1024;
-constexpr int kCountSlices = kCountThreads / 128;
-
-template <int G, typename E>
-__global__ __launch_bounds__(kCountThreads) void bern_counts_kernel(Params p) {
-    __shared__ double s_m[128];
-    __shared__ double s_max[kCountThreads / 64];
-    __shared__ int s_cnt[kCountSlices][128];
-    const int grp = blockIdx.x;
-    const int b = grp / p.Hkv, g = grp - b * p.Hkv;
-    const int i = threadIdx.x & 127, slice = threadIdx.x >> 7;
-    double m = 0.0;
-    if (slice == 0 && i < p.D) {
-        float qv[G];
-        m = mean_abs_query<G, E>(p, b, g, i, qv);
-        s_m[i] = m;
+// How many of the B stratified draws keep a feature of keep probability pi:
+// draw n keeps it iff (n + U_n) / B < pi, in fp64.  Whatever U in [0, 1) is,
+// the rounded (n + U) / B lies in [fl(n / B), fl((n + 1) / B)] (rounding is
+// monotone and n + 1 is exact), so draw n is kept for certain when
+// fl((n + 1) / B) < pi and never when fl(n / B) >= pi; only the other draws
+// need their uniform.  With n0 = floor(B pi) (B <= 64, so 1/B dwarfs the
+// rounding) every draw below n0 - 1 is certain and every draw above n0 + 1
+// impossible: at most three draws are looked at, one or two Philox blocks.
+__device__ __forceinline__ int bern_count(double pi, int B, uint64_t seed, int b, int g, int i) {
+    if (!(pi > 0.0)) return 0;
+    const double Bd = (double)B;
+    const int n0 = min((int)floor(Bd * pi), B);
+    int c = max(n0 - 1, 0);
+    const int n1 = min(n0 + 1, B - 1);
+    for (int n = max(n0 - 1, 0); n <= n1; ++n) {
+        if ((double)(n + 1) / Bd < pi) {
+            ++c;
+        } else if ((double)n / Bd >= pi) {
+            break;                                  // and so are all later draws
+        } else if (((double)n + bern_uniform(seed, b, g, i, n)) / Bd < pi) {
+            ++c;
+        }
     }
-    const double top = block_max_f64(m, kCountThreads / 64, s_max);     // its barriers publish s_m
-    int count = 0;
-    if (i < p.D && top > 0.0) {
-        const double pi = s_m[i] / top;
-        for (int n = slice; n < p.bern_B; n += kCountSlices)
-            if (((double)n + bern_uniform(p.seed, b, g, i, n)) / (double)p.bern_B < pi) ++count;
-    }
-    s_cnt[slice][i] = count;
-    __syncthreads();
-    if (slice == 0 && i < p.D) {
-        int c = 0;
-#pragma unroll
-        for (int k = 0; k < kCountSlices; ++k) c += s_cnt[k][i];
-        p.bern_counts[(int64_t)grp * p.D + i] = (uint8_t)c;
-    }
+    return c;
 }
 
 // The group's kept features and, per head, their weights m_hat_i / m_i * q_{h,i}.
@@ -99,7 +92,8 @@ struct BernFeatures {
     float w[G][128];
 };
 
-// Builds the kept-feature list of the item's group in `bf` (all threads call it).
+// Builds the kept-feature list of the item's group in `bf` (all threads call
+// it); the group's first split also writes the feature counts.
 template <int G, typename E, int NT>
 __device__ __forceinline__ void bern_prologue(const Params& p, const Item& it, BernFeatures<G>& bf) {
     __shared__ double s_max[NT / 64];
@@ -107,13 +101,12 @@ __device__ __forceinline__ void bern_prologue(const Params& p, const Item& it, B
     const int i = threadIdx.x;
     const int lane = i & 63, wave = i >> 6;
     float qv[G];
-    int c = 0;
     double m = 0.0;
-    if (i < p.D) {
-        c = p.bern_counts[((int64_t)it.b * p.Hkv + it.g) * p.D + i];
-        m = mean_abs_query<G, E>(p, it.b, it.g, i, qv);
-    }
+    if (i < p.D) m = mean_abs_query<G, E>(p, it.b, it.g, i, qv);
     const double top = block_max_f64(m, (p.D + 63) / 64, s_max);
+    int c = 0;
+    if (i < p.D && top > 0.0) c = bern_count(m / top, p.bern_B, p.seed, it.b, it.g, i);
+    if (i < p.D && it.t == 0) p.bern_counts[((int64_t)it.b * p.Hkv + it.g) * p.D + i] = (uint8_t)c;
     const bool keep = i < p.D && c > 0;
     const unsigned long long bal = __ballot(keep);
     if (lane == 0 && wave < 2) s_cnt[wave] = __popcll(bal);
@@ -129,30 +122,70 @@ __device__ __forceinline__ void bern_prologue(const Params& p, const Item& it, B
     __syncthreads();
 }
 
-// Estimated scores of the split's keys.  Every lane reads one 16-byte piece
-// of a feature row per kept feature it takes: wave w covers the keys
-// [w * split / NW, (w + 1) * split / NW), lane l the KPL keys from
-// (l mod L) * KPL on (L lanes per row piece), and the 64 / L lane groups of a
-// wave deal the kept features out round-robin (group r takes the r-th, the
-// (r + 64/L)-th, ... in ascending feature order).  Each lane sums its features
-// with fused multiply-adds in that order; the groups' sums are then added
-// pairwise (xor butterfly, the same result in every lane of a key).
-template <int G, typename E, int NT>
+// A piece of KPL consecutive elements of a feature row, as one load.
+template <int BYTES> struct PieceOf;
+template <> struct PieceOf<2> { using T = uint16_t; };
+template <> struct PieceOf<4> { using T = uint32_t; };
+template <> struct PieceOf<8> { using T = uint2; };
+template <> struct PieceOf<16> { using T = uint4; };
+
+template <typename E, int KPL, typename P>
+__device__ __forceinline__ void unpack_piece(const P& v, float (&x)[KPL]) {
+    if constexpr (E::bytes == 2) {
+        if constexpr (KPL == 1) {
+            x[0] = __uint_as_float((uint32_t)v << 16);
+        } else if constexpr (KPL == 2) {
+            x[0] = __uint_as_float(v << 16);
+            x[1] = __uint_as_float(v & 0xFFFF0000u);
+        } else {
+            x[0] = __uint_as_float(v.x << 16);
+            x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+            x[2] = __uint_as_float(v.y << 16);
+            x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        }
+    } else {
+        if constexpr (KPL == 1) {
+            x[0] = __uint_as_float(v);
+        } else if constexpr (KPL == 2) {
+            x[0] = __uint_as_float(v.x);
+            x[1] = __uint_as_float(v.y);
+        } else {
+            x[0] = __uint_as_float(v.x);
+            x[1] = __uint_as_float(v.y);
+            x[2] = __uint_as_float(v.z);
+            x[3] = __uint_as_float(v.w);
+        }
+    }
+}
+
+// Estimated scores of the split's keys.  Wave w covers the keys
+// [w * split / NW, (w + 1) * split / NW), lane l the KPL keys from l * KPL on,
+// and every wave reads the kept feature rows one after the other: one load
+// per lane and feature, the whole wave on the same row, so that the feature
+// index and the G weights are the same in every lane (they are taken from
+// one lane into scalar registers) and the vector registers hold the loads in
+// flight, UF features' worth (about 128 bytes per lane).  The loads carry no
+// branches, so that they all stay in flight: a batch past the last kept
+// feature repeats that feature with weight 0, a lane past the split's keys
+// re-reads the split's first piece, and a piece that the sequence ends inside
+// is read whole (it ends within the row: pieces are KPL-aligned and the row
+// stride is a multiple of KPL elements); the scores of keys past the end are
+// never written.  Each key's score is the fp32 fused multiply-add sum of its
+// kept features in ascending order.
+template <int G, typename E, int NT, int KPL>
 __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, float* sc, const BernFeatures<G>& bf) {
     constexpr int NW = NT / 64;
-    constexpr int KPL = 16 / E::bytes;         // keys per lane: one 16-byte load per feature row
-    constexpr int UF = G * KPL >= 32 ? 4 : 8;  // features a lane has in flight at once (registers)
+    constexpr int PB = KPL * E::bytes;                         // bytes per load
+    constexpr int UF = PB >= 16 ? 8 : PB >= 8 ? 16 : 32;        // features in flight
+    static_assert(UF <= 64, "one lane per feature of a batch");
+    using Piece = typename PieceOf<PB>::T;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int per_wave = p.split / NW;         // 16 .. 256 keys
-    const int L = per_wave / KPL;              // lanes per row piece: 2 .. 64
-    const int nfg = 64 / L;                    // feature groups of the wave
-    const int fg = lane / L;
-    const int lk = wave * per_wave + (lane - fg * L) * KPL;      // first local key of this lane
-    const bool active = lk < it.ns;
-    const bool full = lk + KPL <= it.ns;
-    const char* base = reinterpret_cast<const char*>(p.kt) +
-                       ((int64_t)it.b * p.kt_stride_seq + (int64_t)it.g * p.kt_stride_head + it.key0 +
-                        (active ? lk : 0)) * E::bytes;
+    const int per_wave = p.split / NW;                         // 16 .. 256 keys
+    const int lk = wave * per_wave + lane * KPL;               // first local key of this lane
+    const bool active = lane * KPL < per_wave && lk < it.ns;
+    const char* gbase = reinterpret_cast<const char*>(p.kt) +
+                        ((int64_t)it.b * p.kt_stride_seq + (int64_t)it.g * p.kt_stride_head + it.key0) * E::bytes;
+    const int lane_off = (active ? lk : 0) * E::bytes;
     const int64_t row_bytes = p.kt_stride_feat * E::bytes;
     float acc[G][KPL];
 #pragma unroll
@@ -160,57 +193,34 @@ __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, flo
 #pragma unroll
         for (int j = 0; j < KPL; ++j) acc[h][j] = 0.0f;
     const int nf = bf.n;
-    for (int f0 = fg; f0 < nf; f0 += UF * nfg) {
-        uint4 raw[UF];
+    for (int f0 = 0; f0 < nf; f0 += UF) {
+        // lane u < UF holds the index and weights of feature f0 + u (the last
+        // kept feature with weight 0 past the end)
+        const int fl = min(f0 + lane, nf - 1);
+        const bool real = lane < UF && f0 + lane < nf;
+        const int my_feat = bf.feat[fl];
+        float my_w[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) my_w[h] = real ? bf.w[h][fl] : 0.0f;
+        Piece raw[UF];
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
-            const int f = f0 + u * nfg;
-            raw[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (f < nf && active) {
-                const char* row = base + (int64_t)bf.feat[f] * row_bytes;
-                if (full) {
-                    raw[u] = *reinterpret_cast<const uint4*>(row);
-                } else {
-                    // the sequence ends inside this lane's keys: element by element
-                    uint32_t w4[4] = {0u, 0u, 0u, 0u};
-                    for (int j = 0; lk + j < it.ns; ++j) {
-                        const uint32_t bits = __float_as_uint(E::elem(row, j));
-                        if constexpr (E::bytes == 2)
-                            w4[j >> 1] |= (j & 1) ? (bits & 0xFFFF0000u) : (bits >> 16);
-                        else
-                            w4[j] = bits;
-                    }
-                    raw[u] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-                }
-            }
+            const int feat = __builtin_amdgcn_readlane(my_feat, u);
+            raw[u] = *reinterpret_cast<const Piece*>(gbase + (int64_t)feat * row_bytes + lane_off);
         }
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
-            const int f = f0 + u * nfg;
-            const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
             float x[KPL];
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                if constexpr (E::bytes == 2)
-                    x[j] = __uint_as_float((j & 1) ? (w4[j >> 1] & 0xFFFF0000u) : (w4[j >> 1] << 16));
-                else
-                    x[j] = __uint_as_float(w4[j]);
-            }
+            unpack_piece<E, KPL>(raw[u], x);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float wt = f < nf ? bf.w[h][f] : 0.0f;
+                const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w[h]), u));
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) acc[h][j] = fmaf(wt, x[j], acc[h][j]);
             }
         }
     }
-    for (int off = L; off < 64; off <<= 1) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int j = 0; j < KPL; ++j) acc[h][j] += __shfl_xor(acc[h][j], off, 64);
-    }
-    if (fg == 0 && active) {
+    if (active) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -220,61 +230,74 @@ __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, flo
     priority_tail();
 }
 
-template <int G, typename E, int NT>
-__device__ __forceinline__ void bern_scores(const Params& p, const Item& it, float* sc) {
-    __shared__ BernFeatures<G> bf;
-    bern_prologue<G, E, NT>(p, it, bf);
-    bern_stream<G, E, NT>(p, it, sc, bf);
+// Keys per lane of a split: a wave covers split / 4 of them, 64 lanes.
+inline int bern_kpl(int split) {
+    const int per_lane = split / (kThreads / 64) / 64;
+    return per_lane >= 4 ? 4 : per_lane >= 2 ? 2 : 1;
 }
 
-template <int G, int D, typename E, int NT>
+template <int G, int D, typename E, int NT, int KPL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 3)))
 void bern_fused_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ BernFeatures<G> bf;
     const int item = take_item(p);
     if (item < 0) return;
     priority_streaming();
     const unsigned int err0 = p.sync->error;
-    fused_item<G, D, E, NT>(p, make_item(p, item), err0, smem,
-                            [&](const Item& it, float* sc, const int*) { bern_scores<G, E, NT>(p, it, sc); });
+    const Item it = make_item(p, item);
+    // splits with keys need the feature list; the first split of every group,
+    // keys or not, writes the counts
+    if (it.ns > 0 || it.t == 0) bern_prologue<G, E, NT>(p, it, bf);
+    fused_item<G, D, E, NT>(p, it, err0, smem,
+                            [&](const Item& at, float* sc, const int*) { bern_stream<G, E, NT, KPL>(p, at, sc, bf); });
 }
 
-template <int G, int D, typename E, int NT>
+template <int G, int D, typename E, int NT, int KPL>
 __global__ __launch_bounds__(NT) void bern_score_kernel(Params p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ BernFeatures<G> bf;
     const Item it = make_item(p, blockIdx.x);
+    if (it.ns == 0 && it.t != 0) return;
+    bern_prologue<G, E, NT>(p, it, bf);
     if (it.ns == 0) return;
     const LdsLayout L = lds_layout(G, D, p.split, NT);
     float* sc = reinterpret_cast<float*>(smem + L.scratch);
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
-    bern_scores<G, E, NT>(p, it, sc);
+    bern_stream<G, E, NT, KPL>(p, it, sc, bf);
     __syncthreads();
     split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     __syncthreads();
     write_stash<G, NT>(p, it, sc);
 }
 
-template <int G, int D, typename E>
+template <int G, int D, typename E, int KPL>
 static const void* bern_fn(bool fused) {
-    return fused ? reinterpret_cast<const void*>(&bern_fused_kernel<G, D, E, kThreads>)
-                 : reinterpret_cast<const void*>(&bern_score_kernel<G, D, E, kThreads>);
+    return fused ? reinterpret_cast<const void*>(&bern_fused_kernel<G, D, E, kThreads, KPL>)
+                 : reinterpret_cast<const void*>(&bern_score_kernel<G, D, E, kThreads, KPL>);
+}
+
+template <int G, int D, typename E>
+static const void* bern_fn_k(int kpl, bool fused) {
+    return kpl == 4 ? bern_fn<G, D, E, 4>(fused) : kpl == 2 ? bern_fn<G, D, E, 2>(fused) : bern_fn<G, D, E, 1>(fused);
 }
 
 template <int D, typename E>
-static const void* bern_fn_g(int G, bool fused) {
+static const void* bern_fn_g(int G, int kpl, bool fused) {
     switch (G) {
-        case 1: return bern_fn<1, D, E>(fused);
-        case 2: return bern_fn<2, D, E>(fused);
-        case 4: return bern_fn<4, D, E>(fused);
-        case 7: return bern_fn<7, D, E>(fused);
-        case 8: return bern_fn<8, D, E>(fused);
+        case 1: return bern_fn_k<1, D, E>(kpl, fused);
+        case 2: return bern_fn_k<2, D, E>(kpl, fused);
+        case 4: return bern_fn_k<4, D, E>(kpl, fused);
+        case 7: return bern_fn_k<7, D, E>(kpl, fused);
+        case 8: return bern_fn_k<8, D, E>(kpl, fused);
         default: return nullptr;
     }
 }
 
 static const void* bern_function(const Params& p, int dtype, bool fused) {
-    if (dtype == 0) return p.D == 64 ? bern_fn_g<64, Bf16>(p.G, fused) : bern_fn_g<128, Bf16>(p.G, fused);
-    return p.D == 64 ? bern_fn_g<64, F32>(p.G, fused) : bern_fn_g<128, F32>(p.G, fused);
+    const int kpl = bern_kpl(p.split);
+    if (dtype == 0) return p.D == 64 ? bern_fn_g<64, Bf16>(p.G, kpl, fused) : bern_fn_g<128, Bf16>(p.G, kpl, fused);
+    return p.D == 64 ? bern_fn_g<64, F32>(p.G, kpl, fused) : bern_fn_g<128, F32>(p.G, kpl, fused);
 }
 
 static hipError_t launch_bern(const Params& p, int dtype, hipStream_t stream, bool fused) {
@@ -298,28 +321,6 @@ int bern_fused_blocks_per_cu(const Params& p, int dtype) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, lds) != hipSuccess) return 0;
     return n;
-}
-
-template <int G, typename E>
-static hipError_t launch_counts_t(const Params& p, hipStream_t stream) {
-    hipLaunchKernelGGL((bern_counts_kernel<G, E>), dim3((unsigned)(p.B * p.Hkv)), dim3(kCountThreads), 0, stream, p);
-    return hipGetLastError();
-}
-
-template <typename E>
-static hipError_t launch_counts_e(const Params& p, hipStream_t stream) {
-    switch (p.G) {
-        case 1: return launch_counts_t<1, E>(p, stream);
-        case 2: return launch_counts_t<2, E>(p, stream);
-        case 4: return launch_counts_t<4, E>(p, stream);
-        case 7: return launch_counts_t<7, E>(p, stream);
-        case 8: return launch_counts_t<8, E>(p, stream);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_bern_counts(const Params& p, int dtype, hipStream_t stream) {
-    return dtype == 0 ? launch_counts_e<Bf16>(p, stream) : launch_counts_e<F32>(p, stream);
 }
 
 }  // namespace santa

@@ -111,7 +111,6 @@ hipError_t launch_score(const Params& p, int dtype, hipStream_t stream, bool sta
 hipError_t launch_topk(const Params& p, int dtype, hipStream_t stream);
 // Bernoulli qK^T: the feature counts, then the fused kernel (grid p.items, items
 // by ticket when p.use_ticket) or the score pass of the two-kernel path
-hipError_t launch_bern_counts(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_bern_fused(const Params& p, int dtype, hipStream_t stream);
 hipError_t launch_bern_score(const Params& p, int dtype, hipStream_t stream);
 int bern_fused_blocks_per_cu(const Params& p, int dtype);

@@ -7,16 +7,16 @@ against oracle/bernoulli.py through the C ABI.
   estimated scores, except for targets within a CDF window of an interval
   edge.  The window is 1e-6 (the exact path's) plus twice the p-weighted bound
   on the GPU's fp32 score error.  The library states its summation: the
-  weights are rounded once to fp32, the kept features (ascending) are dealt
-  round-robin to F lane groups (F a power of two up to 32, fixed by the split
-  size), each group sums its terms by fused multiply-adds and the F group sums
-  are added pairwise.  To first order the error of key j's score is then at
-  most 2^-24 times (the sum of |w_f k_jf| for the weights' rounding, plus the
-  magnitudes of every group's running sums, plus log2(F) times the sum of
-  |w_f k_jf| for the pairwise additions); the test takes the largest of these
-  over every F, divides by sqrt(d) and adds the rounding of the 1/sqrt(d)
-  scale.  A CDF moves by at most twice the p-weighted mean of the scores'
-  errors.
+  weights are rounded once to fp32 and each score sums its kept features'
+  terms by fused multiply-adds in ascending feature order.  The bound below
+  also covers the same sum split round-robin over F lane groups whose sums are
+  added pairwise (F a power of two up to 32; F = 1 is the sequential sum): to
+  first order the error of key j's score is at most 2^-24 times (the sum of
+  |w_f k_jf| for the weights' rounding, plus the magnitudes of every group's
+  running sums, plus log2(F) times the sum of |w_f k_jf| for the pairwise
+  additions); the test takes the largest of these over every F, divides by
+  sqrt(d) and adds the rounding of the 1/sqrt(d) scale.  A CDF moves by at
+  most twice the p-weighted mean of the scores' errors.
 * o lies within 1e-3 relative L2 of the fp64 gather-mean of the GPU's own
   indices.
 
