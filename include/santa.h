@@ -355,6 +355,85 @@ santa_status santa_decode_bernoulli(const santa_shape* shape, const void* q, con
                                     float* o, int32_t* idx, uint8_t* feature_counts, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * SANTA++: attention through representative keys ("SANTA++: Sampling
+ * Attention through Representative Keys", section 2.2-2.3; Appendix A,
+ * Algorithms 1, 2 and 4; Appendix D).
+ *
+ * After prefill, the N prompt keys of every (sequence, KV head) are cut into
+ * contiguous parents of P tokens (Algorithm 4).  In each parent, up to R
+ * actual keys become representatives: the first is the member nearest the
+ * parent's mean key, each later one the member farthest from its nearest
+ * representative so far (ties to the lower token index); every member joins
+ * its nearest representative's team (ties to the earlier representative) and
+ * each representative owns its own row (Algorithm 2).  Distances are squared
+ * Euclidean in fp64 on the keys as stored.  Teams are numbered parent by
+ * parent, in the order their representatives were chosen; members keep token
+ * order.  A parent of c tokens holds min(R, c) teams, so there are
+ * M = (N / P) R + min(R, N mod P) teams (santa_pp_num_teams).
+ *
+ * Team table (caller-owned device arrays, written by santa_pp_build and read
+ * by santa_pp_decode; B, Hkv, d from the shape, dtype of the caches):
+ *   packed_k, packed_v  [B, Hkv, N, d]  the prompt rows in team order (team
+ *                       g's members are rows team_start[g] .. team_start[g+1]-1)
+ *   rep_k               [B, Hkv, M, d]  the representative keys
+ *   team_start          [B, Hkv, M + 1] int32
+ *   perm                [B, Hkv, N]     int32: token index of each packed row
+ * Limits: 1 <= R <= P <= 64, P divisible by R, 1 <= N <= max_seq_len,
+ * M <= 131072; contiguous caches only (page_size 0).
+ */
+typedef struct santa_pp_table {
+    void* packed_k;
+    void* packed_v;
+    void* rep_k;
+    int32_t* team_start;
+    int32_t* perm;
+} santa_pp_table;
+
+/* M for a prompt of N tokens, parents of P and at most R teams each; -1 if the
+ * parameters are invalid (R > P, P not divisible by R, N < 1). */
+int32_t santa_pp_num_teams(int32_t N, int32_t P, int32_t R);
+
+/* Builds the team table from the first N rows of every sequence of the
+ * token-major k_cache / v_cache (layout of shape).  Asynchronous on stream. */
+santa_status santa_pp_build(const santa_shape* shape, const void* k_cache, const void* v_cache, int32_t N,
+                            int32_t P, int32_t R, const santa_pp_table* table, void* stream);
+
+/* Workspace bytes of santa_pp_decode for K teams per query head.  The
+ * workspace must be zero-filled once (santa_workspace_init); every completed
+ * call leaves its counters at zero. */
+santa_status santa_pp_workspace_size(const santa_shape* shape, int32_t N, int32_t P, int32_t R, int32_t K,
+                                     size_t* bytes);
+
+/*
+ * One SANTA++ decode step (Algorithm 1 for every query head; section 2.3).
+ * For query head h of sequence b (KV head g = h / G):
+ *   phi_t = log n_t + q . l_t / sqrt(d)                     (Eq. 3, fp32)
+ *   Y_t   = phi_t + G_t, G_t = -log(-log U), U = ((w0 >> 11) + 1/2) 2^-53,
+ *           w0 word 0 of Philox4x64-10 with key (seed, 2) and counter
+ *           (t, h, b, 0)                                    (fp64, added in fp32)
+ *   the K teams of largest Y (ties to the lower team index) and tau, the
+ *   (K+1)-th largest; c_t = 1 - exp(-exp(phi_t - tau))      (Eq. 7, fp64)
+ *   o = U_hat / Z_hat over the suffix rows N .. seq_len-1 of the caches
+ *   (weight 1) and every member of the selected teams (weight 1 / c_t),
+ *   exponentials of s = q . k / sqrt(d)                     (Eq. 4, fp32)
+ * K >= M selects every team with c = 1 (dense attention).  The heads of a GQA
+ * group read the union of their teams once (Appendix D).
+ *
+ *   q         [B, Hq, d]; k_cache, v_cache token-major, for the suffix rows;
+ *   seq_lens  [B] int32 device: prompt + generated rows (below N counts as N)
+ *   o         [B, Hq, d] fp32
+ *   teams     [B, Hq, K + 1] int32: the selected teams in ascending order, then
+ *             the threshold team (-1 entries past min(K, M) and for K >= M)
+ *   corr      [B, Hq, K] fp32: c_t of teams[j] (1 for K >= M)
+ * Workspace: santa_pp_workspace_size bytes, 256-byte aligned.  Three launches
+ * on stream: routing, selection (with the group's read plan) and attention.
+ */
+santa_status santa_pp_decode(const santa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, int32_t N, int32_t P, int32_t R, const santa_pp_table* table,
+                             int32_t K, uint64_t seed, float* o, int32_t* teams, float* corr, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Algorithms of santa_args. */
 enum {
     SANTA_ALGO_PROP = 0,    /* santa_decode: exact global budget (section 3.2, S2ANTA-prop) */

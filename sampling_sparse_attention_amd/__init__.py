@@ -22,7 +22,8 @@ __all__ = [
     "workspace_error", "validate", "Args", "santa_decode_args", "santa_workspace_status",
     "ALGO_PROP", "ALGO_FLASH", "FLAG_TWO_KERNEL", "santa_decode_noalloc", "santa_noalloc_init",
     "santa_noalloc_status", "santa_noalloc_scratch_bytes", "santa_decode_topk",
-    "KtLayout", "santa_decode_bernoulli", "EXPORTED_SYMBOLS",
+    "KtLayout", "santa_decode_bernoulli", "PPTable", "santa_pp_num_teams", "allocate_pp_table",
+    "santa_pp_build", "santa_pp_workspace_size", "santa_pp_decode", "EXPORTED_SYMBOLS",
 ]
 
 MODE_MULTINOMIAL = 0
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "santa_decode_args", "santa_workspace_status",
     "santa_noalloc_scratch_bytes", "santa_noalloc_init", "santa_decode_noalloc", "santa_noalloc_status",
     "santa_decode_topk", "santa_decode_bernoulli",
+    "santa_pp_num_teams", "santa_pp_build", "santa_pp_workspace_size", "santa_pp_decode",
 )
 ALGO_PROP = 0
 ALGO_FLASH = 1
@@ -92,6 +94,12 @@ class KtLayout(ctypes.Structure):
     _fields_ = [("stride_seq", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("stride_feat", ctypes.c_int64)]
 
 
+class PPTable(ctypes.Structure):
+    """Mirror of ``santa_pp_table``."""
+    _fields_ = [("packed_k", ctypes.c_void_p), ("packed_v", ctypes.c_void_p), ("rep_k", ctypes.c_void_p),
+                ("team_start", ctypes.c_void_p), ("perm", ctypes.c_void_p)]
+
+
 class SantaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__(f"{where}: {detail} (status {status})")
@@ -133,6 +141,15 @@ def library() -> ctypes.CDLL:
         lib.santa_decode_bernoulli.restype = ctypes.c_int
         lib.santa_decode_bernoulli.argtypes = [ctypes.POINTER(Shape), vp, vp, ctypes.POINTER(KtLayout), vp, vp,
                                                i32, i32, u64, i32, vp, vp, vp, vp, sz, vp]
+        lib.santa_pp_num_teams.restype = i32
+        lib.santa_pp_num_teams.argtypes = [i32, i32, i32]
+        lib.santa_pp_build.restype = ctypes.c_int
+        lib.santa_pp_build.argtypes = [ctypes.POINTER(Shape), vp, vp, i32, i32, i32, ctypes.POINTER(PPTable), vp]
+        lib.santa_pp_workspace_size.restype = ctypes.c_int
+        lib.santa_pp_workspace_size.argtypes = [ctypes.POINTER(Shape), i32, i32, i32, i32, ctypes.POINTER(sz)]
+        lib.santa_pp_decode.restype = ctypes.c_int
+        lib.santa_pp_decode.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, i32, i32, i32, ctypes.POINTER(PPTable),
+                                        i32, u64, vp, vp, vp, vp, sz, vp]
         lib.santa_noalloc_scratch_bytes.argtypes = []
         lib.santa_noalloc_init.restype = ctypes.c_int
         lib.santa_noalloc_init.argtypes = [vp]
@@ -375,6 +392,81 @@ def santa_decode_bernoulli(shape, q, k_t, v_cache, seq_lens, num_samples, mode, 
                                             _ptr(idx), _ptr(feature_counts), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "santa_decode_bernoulli")
+
+
+def santa_pp_num_teams(N: int, P: int, R: int) -> int:
+    """Teams of a prompt of N tokens, contiguous parents of P, at most R teams each (-1: invalid)."""
+    return int(library().santa_pp_num_teams(int(N), int(P), int(R)))
+
+
+def allocate_pp_table(shape: Shape, N: int, P: int, R: int, dtype: torch.dtype, device) -> dict:
+    """The device arrays of a SANTA++ team table (``santa_pp_table``) for ``shape``."""
+    M = santa_pp_num_teams(N, P, R)
+    if M < 1:
+        raise ValueError(f"invalid team parameters N={N}, P={P}, R={R}")
+    B, Hkv, d = shape.batch, shape.num_kv_heads, shape.head_dim
+    return {"packed_k": torch.empty((B, Hkv, N, d), dtype=dtype, device=device),
+            "packed_v": torch.empty((B, Hkv, N, d), dtype=dtype, device=device),
+            "rep_k": torch.empty((B, Hkv, M, d), dtype=dtype, device=device),
+            "team_start": torch.empty((B, Hkv, M + 1), dtype=torch.int32, device=device),
+            "perm": torch.empty((B, Hkv, N), dtype=torch.int32, device=device),
+            "N": N, "P": P, "R": R, "M": M}
+
+
+def _pp_table(shape: Shape, table: dict, dtype, device) -> PPTable:
+    B, Hkv, d = shape.batch, shape.num_kv_heads, shape.head_dim
+    N, M = table["N"], table["M"]
+    want = {"packed_k": ((B, Hkv, N, d), dtype), "packed_v": ((B, Hkv, N, d), dtype),
+            "rep_k": ((B, Hkv, M, d), dtype), "team_start": ((B, Hkv, M + 1), torch.int32),
+            "perm": ((B, Hkv, N), torch.int32)}
+    for name, (shp, dt) in want.items():
+        t = table[name]
+        if not isinstance(t, torch.Tensor) or tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous() \
+                or t.device != device:
+            raise ValueError(f"team table {name} must be a contiguous {dt} {shp} tensor on {device}")
+    return PPTable(*(table[name].data_ptr() for name in ("packed_k", "packed_v", "rep_k", "team_start", "perm")))
+
+
+def santa_pp_build(shape, k_cache, v_cache, table: dict, stream=None) -> None:
+    """Builds the SANTA++ team table from the first ``table["N"]`` rows of every
+    sequence (``santa_pp_build`` of the C ABI)."""
+    if k_cache.dtype not in _DTYPE_CODE or v_cache.dtype != k_cache.dtype or v_cache.stride() != k_cache.stride() \
+            or v_cache.shape != k_cache.shape or k_cache.stride(-1) != 1 or k_cache.dim() != 4:
+        raise ValueError("k_cache and v_cache must be [B, n_max, Hkv, d] of one dtype and layout")
+    if shape.dtype != _DTYPE_CODE[k_cache.dtype] or tuple(k_cache.stride()[:3]) != \
+            (shape.kv_stride_seq, shape.kv_stride_tok, shape.kv_stride_head):
+        raise ValueError("shape does not describe k_cache")
+    if k_cache.shape[0] < shape.batch or k_cache.shape[1] < shape.max_seq_len:
+        raise ValueError("k_cache is smaller than the shape")
+    tb = _pp_table(shape, table, k_cache.dtype, k_cache.device)
+    _check(library().santa_pp_build(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache), int(table["N"]),
+                                    int(table["P"]), int(table["R"]), ctypes.byref(tb), _stream_handle(stream)),
+           "santa_pp_build")
+
+
+def santa_pp_workspace_size(shape: Shape, N: int, P: int, R: int, K: int) -> int:
+    out = ctypes.c_size_t()
+    _check(library().santa_pp_workspace_size(ctypes.byref(shape), int(N), int(P), int(R), int(K), ctypes.byref(out)),
+           "santa_pp_workspace_size")
+    return out.value
+
+
+def santa_pp_decode(shape, q, k_cache, v_cache, seq_lens, table: dict, K, seed, o, teams, corr, workspace,
+                    stream=None) -> None:
+    """One SANTA++ decode step (``santa_pp_decode`` of the C ABI): ``o`` [B, Hq, d],
+    ``teams`` [B, Hq, K + 1] int32 (selected teams ascending, then the threshold
+    team), ``corr`` [B, Hq, K] fp32 inclusion corrections."""
+    validate(shape, q, k_cache, v_cache, seq_lens, None, int(K) + 1, o, teams, workspace)
+    B, Hq, _ = q.shape
+    if not isinstance(corr, torch.Tensor) or corr.dtype != torch.float32 or tuple(corr.shape) != (B, Hq, int(K)) \
+            or not corr.is_contiguous() or corr.device != q.device:
+        raise ValueError(f"corr must be a contiguous float32 [{B}, {Hq}, {K}] tensor on q's device")
+    tb = _pp_table(shape, table, q.dtype, q.device)
+    _check(library().santa_pp_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                     int(table["N"]), int(table["P"]), int(table["R"]), ctypes.byref(tb), int(K),
+                                     ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(o), _ptr(teams), _ptr(corr),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream)), "santa_pp_decode")
 
 
 def santa_noalloc_scratch_bytes() -> int:

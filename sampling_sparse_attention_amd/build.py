@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["santa_abi.hip", "santa_score.hip", "santa_sample.hip", "santa_fused.hip", "santa_flash.hip",
-           "santa_topk.hip", "santa_bernoulli.hip"]
+           "santa_topk.hip", "santa_bernoulli.hip", "santa_pp.hip"]
 
 COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",

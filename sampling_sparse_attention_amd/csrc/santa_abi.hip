@@ -9,6 +9,7 @@
 
 #include "santa.h"
 #include "santa_internal.h"
+#include "santa_pp.h"
 
 namespace {
 
@@ -321,6 +322,93 @@ santa_status noalloc_scratch(bool clear, hipStream_t stream, void** out) {
     return SANTA_STATUS_OK;
 }
 
+
+// ---------------------------------------------------------------------------
+// SANTA++
+// ---------------------------------------------------------------------------
+int64_t pp_teams(int64_t N, int64_t P, int64_t R) {
+    if (N < 1 || P < 1 || R < 1 || R > P || P % R) return -1;
+    return (N / P) * R + (N % P ? std::min<int64_t>(R, N % P) : 0);
+}
+
+struct PPLayout {
+    size_t arrive, done, y, phi, plan, plan_logc, plan_n, part, total;
+};
+
+PPLayout pp_layout(const santa_shape& s, int G, int64_t M, int64_t Keff) {
+    const int64_t Mpad = (M + 3) & ~int64_t(3);
+    const int64_t PL = std::min<int64_t>(M, (int64_t)G * Keff);
+    const int64_t groups = (int64_t)s.batch * s.num_kv_heads;
+    const int64_t rows = (int64_t)s.batch * s.num_q_heads;
+    PPLayout L;
+    size_t at = 0;
+    auto take = [&](size_t bytes) { const size_t r = at; at = align256(at + bytes); return r; };
+    L.arrive = take(groups * 4);
+    L.done = take(groups * 4);
+    L.y = take(rows * Mpad * 4);
+    L.phi = take(rows * Mpad * 4);
+    L.plan = take(groups * PL * 4);
+    L.plan_logc = take(groups * PL * G * 4);
+    L.plan_n = take(groups * 4);
+    L.part = take(rows * santa::kPPChunks * (int64_t)(s.head_dim + 2) * 4);
+    L.total = at;
+    return L;
+}
+
+// Shape, prompt and team checks shared by the SANTA++ entry points.
+santa_status pp_check(const santa_shape* s, int32_t N, int32_t P, int32_t R, int* G, int64_t* M) {
+    Plan plan;
+    santa_status st = make_plan(s, 1, SANTA_MODE_SYSTEMATIC, &plan);
+    if (st != SANTA_STATUS_OK) return st;
+    if (s->page_size != 0) return fail(SANTA_STATUS_UNSUPPORTED, "SANTA++ reads a contiguous cache (page_size must be 0)");
+    if (P < 1 || P > santa::kPPMaxParent || R < 1 || R > P || P % R)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "need 1 <= R <= P <= %d with P divisible by R (P %d, R %d)",
+                    santa::kPPMaxParent, P, R);
+    if (N < 1 || N > s->max_seq_len)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "prompt length %d not in [1, max_seq_len %d]", N, s->max_seq_len);
+    const int64_t m = pp_teams(N, P, R);
+    if (m > santa::kPPMaxTeams)
+        return fail(SANTA_STATUS_UNSUPPORTED, "%lld teams, at most %d", (long long)m, santa::kPPMaxTeams);
+    *G = plan.G;
+    *M = m;
+    return SANTA_STATUS_OK;
+}
+
+santa_status pp_table_check(const santa_pp_table* t) {
+    if (!t || !t->packed_k || !t->packed_v || !t->rep_k || !t->team_start || !t->perm)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "a team-table pointer is NULL");
+    if (!aligned(t->packed_k, 16) || !aligned(t->packed_v, 16) || !aligned(t->rep_k, 16) ||
+        !aligned(t->team_start, 4) || !aligned(t->perm, 4))
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "team-table arrays must be 16-byte (rows) or 4-byte (indices) aligned");
+    return SANTA_STATUS_OK;
+}
+
+void pp_fill(santa::PPParams* p, const santa_shape* s, int G, int32_t N, int32_t P, int32_t R, int64_t M,
+             const santa_pp_table* t) {
+    *p = santa::PPParams{};
+    p->B = s->batch;
+    p->Hq = s->num_q_heads;
+    p->Hkv = s->num_kv_heads;
+    p->G = G;
+    p->D = s->head_dim;
+    p->N = N;
+    p->P = P;
+    p->R = R;
+    p->M = (int)M;
+    p->Mpad = (int)((M + 3) & ~int64_t(3));
+    p->n_max = s->max_seq_len;
+    p->stride_seq = s->kv_stride_seq;
+    p->stride_tok = s->kv_stride_tok;
+    p->stride_head = s->kv_stride_head;
+    p->packed_k = t->packed_k;
+    p->packed_v = t->packed_v;
+    p->rep_k = t->rep_k;
+    p->team_start = t->team_start;
+    p->perm = t->perm;
+    p->scale = (float)(1.0 / __builtin_sqrt((double)s->head_dim));
+    p->NC = santa::kPPChunks;
+}
+
 }  // namespace
 
 extern "C" {
@@ -598,6 +686,96 @@ santa_status santa_sample_pass(const santa_shape* shape, const void* q, const vo
                                void* workspace, size_t workspace_bytes, void* stream) {
     return run(kSample, shape, q, k_cache, v_cache, seq_lens, block_table, num_samples, mode, seed,
                o, idx, workspace, workspace_bytes, stream);
+}
+
+
+int32_t santa_pp_num_teams(int32_t N, int32_t P, int32_t R) {
+    const int64_t m = pp_teams(N, P, R);
+    return m < 0 || m > INT32_MAX ? -1 : (int32_t)m;
+}
+
+santa_status santa_pp_build(const santa_shape* shape, const void* k_cache, const void* v_cache, int32_t N,
+                            int32_t P, int32_t R, const santa_pp_table* table, void* stream) {
+    int G = 0;
+    int64_t M = 0;
+    santa_status st = pp_check(shape, N, P, R, &G, &M);
+    if (st != SANTA_STATUS_OK) return st;
+    if (!k_cache || !v_cache) return fail(SANTA_STATUS_INVALID_ARGUMENT, "k_cache or v_cache is NULL");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "k_cache and v_cache must be 16-byte aligned");
+    st = pp_table_check(table);
+    if (st != SANTA_STATUS_OK) return st;
+    santa::PPParams p;
+    pp_fill(&p, shape, G, N, P, R, M, table);
+    p.k = k_cache;
+    p.v = v_cache;
+    st = hip_check(santa::launch_pp_build(p, shape->dtype, static_cast<hipStream_t>(stream)), "launching the team build");
+    if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_pp_workspace_size(const santa_shape* shape, int32_t N, int32_t P, int32_t R, int32_t K,
+                                     size_t* bytes) {
+    int G = 0;
+    int64_t M = 0;
+    santa_status st = pp_check(shape, N, P, R, &G, &M);
+    if (st != SANTA_STATUS_OK) return st;
+    if (K < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "the team count K must be >= 1 (got %d)", K);
+    if (!bytes) return fail(SANTA_STATUS_INVALID_ARGUMENT, "bytes is NULL");
+    *bytes = pp_layout(*shape, G, M, std::min<int64_t>(K, M)).total;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
+}
+
+santa_status santa_pp_decode(const santa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, int32_t N, int32_t P, int32_t R, const santa_pp_table* table,
+                             int32_t K, uint64_t seed, float* o, int32_t* teams, float* corr, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    int G = 0;
+    int64_t M = 0;
+    santa_status st = pp_check(shape, N, P, R, &G, &M);
+    if (st != SANTA_STATUS_OK) return st;
+    if (K < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "the team count K must be >= 1 (got %d)", K);
+    if (!q || !k_cache || !v_cache || !seq_lens || !o || !teams || !corr || !workspace)
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "a required pointer is NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+        !aligned(seq_lens, 4) || !aligned(teams, 4) || !aligned(corr, 4))
+        return fail(SANTA_STATUS_INVALID_ARGUMENT, "q, the caches and o must be 16-byte, the index arrays 4-byte aligned");
+    if (!aligned(workspace, 256)) return fail(SANTA_STATUS_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    st = pp_table_check(table);
+    if (st != SANTA_STATUS_OK) return st;
+    const int64_t Keff = std::min<int64_t>(K, M);
+    const PPLayout L = pp_layout(*shape, G, M, Keff);
+    if (workspace_bytes < L.total)
+        return fail(SANTA_STATUS_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    santa::PPParams p;
+    pp_fill(&p, shape, G, N, P, R, M, table);
+    char* w = static_cast<char*>(workspace);
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.seq_lens = seq_lens;
+    p.seed = seed;
+    p.K = K;
+    p.Keff = (int)Keff;
+    p.PL = (int)std::min<int64_t>(M, (int64_t)G * Keff);
+    p.o = o;
+    p.teams = teams;
+    p.corr = corr;
+    p.arrive = reinterpret_cast<unsigned int*>(w + L.arrive);
+    p.done = reinterpret_cast<unsigned int*>(w + L.done);
+    p.y = reinterpret_cast<float*>(w + L.y);
+    p.phi = reinterpret_cast<float*>(w + L.phi);
+    p.plan = reinterpret_cast<int32_t*>(w + L.plan);
+    p.plan_logc = reinterpret_cast<float*>(w + L.plan_logc);
+    p.plan_n = reinterpret_cast<int32_t*>(w + L.plan_n);
+    p.part = reinterpret_cast<float*>(w + L.part);
+    st = hip_check(santa::launch_pp_decode(p, shape->dtype, static_cast<hipStream_t>(stream)),
+                   "launching the SANTA++ decode");
+    if (st != SANTA_STATUS_OK) return st;
+    g_error[0] = '\0';
+    return SANTA_STATUS_OK;
 }
 
 }  // extern "C"

@@ -18,37 +18,14 @@
 //      the kept keys are written to idx in ascending order, their weights to
 //      LDS, and the stash is returned to zero;
 //   4. o = sum_kept exp(s - M) v / sum_kept exp(s - M).
+#include "santa_select.h"
 #include "santa_split.h"
 
 namespace santa {
 
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreads = kSelectBins / 2;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkBins = 2048;
-
-// An order-preserving key: a larger score has a larger key (-0 and +0 are
-// one score, as they compare equal).
-__device__ __forceinline__ uint32_t score_key(float s) {
-    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive sum over the workgroup of each thread's value (all threads take part).
-__device__ __forceinline__ int block_exclusive_sum(int v, int* scratch) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int incl = wave_scan_add_i32(v);
-    if (lane == 63) scratch[wave] = incl;
-    __syncthreads();
-    if (wave == 0) {
-        const int t = lane < kTopkWaves ? scratch[lane] : 0;
-        const int ti = wave_scan_add_i32(t);
-        if (lane < kTopkWaves) scratch[kTopkWaves + lane] = ti - t;
-    }
-    __syncthreads();
-    const int r = scratch[kTopkWaves + wave] + incl - v;
-    __syncthreads();        // scratch is reused by the next call
-    return r;
-}
+constexpr int kTopkBins = kSelectBins;
 
 // Element offset of V row `key` of KV head g of sequence b.
 __device__ __forceinline__ int64_t v_row(const Params& p, int b, int g, int key) {
@@ -107,48 +84,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params p) {
     __syncthreads();
 
     // 2. radix passes: the k-th largest key, digit by digit from the top
-    uint32_t prefix = 0, pmask = 0;
-    int krem = k;                           // keys still to take at or below the current prefix
-    constexpr int kShift[3] = {21, 10, 0};
-    constexpr int kBits[3] = {11, 11, 10};
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = kShift[pass];
-        const uint32_t dmask = (1u << kBits[pass]) - 1u;
-        for (int j = tid; j < kTopkBins; j += kTopkThreads) hist[j] = 0u;
-        __syncthreads();
-        for (int i = i0; i < i1; i += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(row + i);
-            const float sv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t key = score_key(sv[e]);
-                if (i + e < i1 && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-            }
-        }
-        __syncthreads();
-        // thread t owns bins 2t and 2t + 1; the keys in the bins above a bin come
-        // before it, so bin c holds the krem-th largest key when the count above
-        // it is below krem and the count above it plus its own reaches krem
-        const int c_hi = (int)hist[2 * tid + 1], c_lo = (int)hist[2 * tid];
-        const int upto = block_exclusive_sum(c_hi + c_lo, scan) + c_hi + c_lo;    // bins <= 2t + 1
-        if (tid == kTopkThreads - 1) scan[2 * kTopkWaves] = upto;                  // all bins
-        __syncthreads();
-        const int suf = scan[2 * kTopkWaves] - upto;                               // bins > 2t + 1
-        if (suf < krem && krem <= suf + c_hi) {
-            scan[2 * kTopkWaves + 1] = 2 * tid + 1;
-            scan[2 * kTopkWaves + 2] = krem - suf;
-        } else if (suf + c_hi < krem && krem <= suf + c_hi + c_lo) {
-            scan[2 * kTopkWaves + 1] = 2 * tid;
-            scan[2 * kTopkWaves + 2] = krem - suf - c_hi;
-        }
-        __syncthreads();
-        const uint32_t bin = (uint32_t)scan[2 * kTopkWaves + 1];
-        krem = scan[2 * kTopkWaves + 2];
-        prefix |= (bin & dmask) << shift;
-        pmask |= dmask << shift;
-        __syncthreads();
-    }
+    int krem = 0;
+    const uint32_t prefix = radix_kth<kTopkThreads>(row, i0, i1, k, hist, scan, &krem);
     // prefix is the k-th largest key; krem keys equal to it are kept (the lowest indices)
     const uint32_t kth = prefix;
 
@@ -166,9 +103,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params p) {
             }
         }
     }
-    const int eq_before = block_exclusive_sum(n_eq, scan);
+    const int eq_before = block_exclusive_sum<kTopkThreads>(n_eq, scan);
     const int take_eq = max(0, min(n_eq, krem - eq_before));
-    int pos = block_exclusive_sum(n_gt + take_eq, scan);
+    int pos = block_exclusive_sum<kTopkThreads>(n_gt + take_eq, scan);
     float wsum = 0.0f;
     int eq_seen = 0;
     for (int i = i0; i < i1; i += 4) {

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared_functions()
-    assert len(declared) == 19
+    assert len(declared) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", santa.library_path], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (santa_\w+)", out))
@@ -270,6 +270,45 @@ def test_bernoulli_validates_before_touching_the_device(lib):
     paged = _shape(max_seq_len=1024, page_size=16, pages_per_seq=64, num_pages=64)
     assert lib.santa_decode_bernoulli(ctypes.byref(paged), fake, fake, ctypes.byref(good), fake, fake, 64, 2,
                                       ctypes.c_uint64(0), 8, fake, fake, fake, fake, need, None) == INVALID
+
+
+def test_santapp_team_count_and_validation_before_touching_the_device(lib):
+    """santa_pp_num_teams is Algorithm 4's count; the SANTA++ entry points check their
+    parameters, the cache kind and the workspace on the host."""
+    assert santa.santa_pp_num_teams(32768, 16, 4) == 8192
+    assert santa.santa_pp_num_teams(1000, 16, 4) == 62 * 4 + 4          # last parent of 8 tokens: 4 teams
+    assert santa.santa_pp_num_teams(1001, 16, 4) == 62 * 4 + 4
+    assert santa.santa_pp_num_teams(995, 16, 4) == 62 * 4 + 3           # last parent of 3 tokens
+    assert santa.santa_pp_num_teams(10, 4, 4) == 10
+    assert santa.santa_pp_num_teams(10, 16, 3) == -1 and santa.santa_pp_num_teams(10, 2, 4) == -1
+    shape = _shape(max_seq_len=1024, kv_stride_seq=1024 * 8 * 128)
+    fake = ctypes.c_void_p(1 << 20)
+    tb = santa.PPTable(1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    build = lib.santa_pp_build
+    assert build(ctypes.byref(shape), fake, fake, 1000, 16, 3, ctypes.byref(tb), None) == INVALID
+    assert build(ctypes.byref(shape), fake, fake, 1000, 128, 4, ctypes.byref(tb), None) == INVALID
+    assert build(ctypes.byref(shape), fake, fake, 2000, 16, 4, ctypes.byref(tb), None) == INVALID     # N > n_max
+    assert build(ctypes.byref(shape), fake, fake, 1000, 16, 4, None, None) == INVALID
+    assert build(ctypes.byref(shape), None, fake, 1000, 16, 4, ctypes.byref(tb), None) == INVALID
+    bad = santa.PPTable(1 << 20, (1 << 20) + 4, 1 << 20, 1 << 20, 1 << 20)
+    assert build(ctypes.byref(shape), fake, fake, 1000, 16, 4, ctypes.byref(bad), None) == INVALID
+    paged = _shape(max_seq_len=1024, page_size=16, pages_per_seq=64, num_pages=64)
+    assert build(ctypes.byref(paged), fake, fake, 1000, 16, 4, ctypes.byref(tb), None) == UNSUPPORTED
+    big = _shape(max_seq_len=262144, kv_stride_seq=262144 * 8 * 128, split_size=1024)
+    assert build(ctypes.byref(big), fake, fake, 262144, 16, 16, ctypes.byref(tb), None) == UNSUPPORTED   # M > 131072
+    need = santa.santa_pp_workspace_size(shape, 1000, 16, 4, 31)
+    assert need > 0
+    with pytest.raises(santa.SantaError):
+        santa.santa_pp_workspace_size(shape, 1000, 16, 4, 0)
+
+    def dec(K=31, ws_bytes=need, ws=fake, q=fake, N=1000):
+        return lib.santa_pp_decode(ctypes.byref(shape), q, fake, fake, fake, N, 16, 4, ctypes.byref(tb), K,
+                                   ctypes.c_uint64(0), fake, fake, fake, ws, ws_bytes, None)
+    assert dec(K=0) == INVALID
+    assert dec(ws_bytes=need - 1) == WS_SMALL
+    assert dec(ws=ctypes.c_void_p((1 << 20) + 16)) == INVALID
+    assert dec(q=None) == INVALID
+    assert dec(N=0) == INVALID
 
 
 def test_workspace_status_validates_before_touching_the_device(lib):

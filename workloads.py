@@ -127,6 +127,10 @@ WORKLOADS = {
     "paged": Workload("paged", batch=64, q_heads=32, kv_heads=8, head_dim=128,
                       seq_len=32768, page_size=16, samples=(256,),
                       modes=(MODE_SYSTEMATIC,)),
+    # SANTA++ (its page, Appendix E): the Qwen-shaped 32K single-sequence layer,
+    # nominal budget S = 124 with P = 16, R = 4 -> K = 31 teams per query head
+    "qwen32k": Workload("qwen32k", batch=1, q_heads=28, kv_heads=4, head_dim=128, seq_len=32768,
+                        samples=(124,), modes=(MODE_SYSTEMATIC,), outlier_channels=8, outlier_scale=6.0),
     # Bernoulli qK^T (section 5.2): the Llama-shaped step with B = 8 draws
     "bern32k": Workload("bern32k", batch=1, q_heads=32, kv_heads=8, head_dim=128,
                         seq_len=32768, samples=(256,), modes=(MODE_SYSTEMATIC,),
