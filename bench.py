@@ -19,7 +19,9 @@ per launch), the HBM bandwidth of a plain device copy measured in the same run,
 the two-kernel path, S^2ANTA-flash and the top-k comparator on the same inputs,
 the Qwen2.5-7B-shaped long-context step (all three sampling rules), Bernoulli
 qK^T (B = 8 draws, with the fraction of key features read) beside the exact step
-on the same inputs, a parity sample of the timed
+on the same inputs, SANTA++ on the Qwen-shaped 32K layer (31 teams per query
+head, with its logical KV access) beside the exact step on the same caches, a
+parity sample of the timed
 configuration against the oracle (boundary cases, largest CDF difference), and
 the CPU oracle timed on a bounded sample of the same workload.
 """
@@ -425,6 +427,68 @@ def bern_line(santa, steps, eager, dev, ncopies):
     return out
 
 
+def pp_line(santa, steps, eager, dev, ncopies):
+    """SANTA++ on the Qwen-shaped 32K layer (K = 31 teams per query head from S = 124,
+    P = 16, R = 4; the team tables are built before timing), beside the exact SANTA
+    step on the same caches.  Logical KV access counts, per KV head, the M
+    representative keys plus the K and V rows of the union of the group's selected
+    teams, over the 2 N rows of a dense read; the algorithmic bytes are those rows."""
+    w = W.WORKLOADS["qwen32k"]
+    P, R = 16, 4
+    N = w.seq_len
+    copies = make_copies(w, ncopies, dev)
+    shape = santa.make_shape(copies[0]["q"], copies[0]["k"], None, max_seq_len=w.seq_len)
+    tables = []
+    for x in copies:
+        t = santa.allocate_pp_table(shape, N, P, R, x["k"].dtype, dev)
+        santa.santa_pp_build(shape, x["k"], x["v"], t)
+        tables.append(t)
+    M = tables[0]["M"]
+    K = min(M, w.samples[0] // (P // R))
+    B, Hq, d = copies[0]["q"].shape
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    teams = torch.empty((B, Hq, K + 1), dtype=torch.int32, device=dev)
+    corr = torch.empty((B, Hq, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(santa.santa_pp_workspace_size(shape, N, P, R, K), dtype=torch.uint8, device=dev)
+
+    def pp(c):
+        x = copies[c % len(copies)]
+        santa.santa_pp_decode(shape, x["q"], x["k"], x["v"], x["seq_lens"], tables[c % len(copies)], K,
+                              w.sample_seed, o, teams, corr, ws)
+
+    for i in range(20):
+        pp(i)
+    t_p, r_p, c_p = timed(pp, steps, eager, ncopies)
+    run = Runner(santa, copies, w.samples[0], w.modes[0], 0)
+    t_e, r_e, c_e = timed(run.step, steps, eager, ncopies)
+    rows_read = []
+    for c in range(ncopies):
+        pp(c)
+        torch.cuda.synchronize()
+        ts = tables[c]["team_start"].cpu()
+        sel = teams.cpu()[:, :, :K]
+        total = 0
+        for b in range(B):
+            for g in range(w.kv_heads):
+                u = torch.unique(sel[b, g * w.group:(g + 1) * w.group].reshape(-1)).long()
+                total += int((ts[b, g, u + 1] - ts[b, g, u]).sum())
+        rows_read.append(total)
+    union_rows = sum(rows_read) / ncopies
+    groups = B * w.kv_heads
+    row = d * w.elem_bytes
+    alg = groups * M * row + 2 * union_rows * row
+    out = {"config": {"batch": B, "q_heads": Hq, "kv_heads": w.kv_heads, "head_dim": d, "prompt_tokens": N,
+                      "parents": "contiguous", "P": P, "R": R, "S": w.samples[0], "teams_per_head": K,
+                      "teams": M, "suffix_rows": 0, "kv_copies": ncopies},
+           "step_us": t_p * 1e6, "calls_timed": c_p, "rounds": round_stats(r_p),
+           "union_rows": union_rows, "logical_kv_access": (groups * M + 2 * union_rows) / (2 * groups * N),
+           "algorithmic_bytes": alg, "achieved_GBs": alg / t_p / 1e9, "frac_of_peak": alg / t_p / 1e9 / PEAK_HBM_GBS,
+           "exact_santa_step_us": t_e * 1e6, "exact_santa_rounds": round_stats(r_e)}
+    del run, copies, tables
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
@@ -544,6 +608,7 @@ def main(argv=None):
         torch.cuda.empty_cache()
         rec["qwen128k"] = qwen_line(santa, min(args.steps, 400), args.eager, dev)
         rec["bernoulli"] = bern_line(santa, min(args.steps, 400), args.eager, dev, ncopies)
+        rec["santa_pp"] = pp_line(santa, min(args.steps, 400), args.eager, dev, ncopies)
         copies = make_copies(w, 1, dev)
         run = Runner(santa, copies, S, mode, args.split)
     if not args.no_cpu_baseline:

@@ -399,9 +399,8 @@ int32_t santa_pp_num_teams(int32_t N, int32_t P, int32_t R);
 santa_status santa_pp_build(const santa_shape* shape, const void* k_cache, const void* v_cache, int32_t N,
                             int32_t P, int32_t R, const santa_pp_table* table, void* stream);
 
-/* Workspace bytes of santa_pp_decode for K teams per query head.  The
- * workspace must be zero-filled once (santa_workspace_init); every completed
- * call leaves its counters at zero. */
+/* Workspace bytes of santa_pp_decode for K teams per query head (any
+ * contents: every call overwrites what it reads). */
 santa_status santa_pp_workspace_size(const santa_shape* shape, int32_t N, int32_t P, int32_t R, int32_t K,
                                      size_t* bytes);
 
@@ -418,7 +417,8 @@ santa_status santa_pp_workspace_size(const santa_shape* shape, int32_t N, int32_
  *   (weight 1) and every member of the selected teams (weight 1 / c_t),
  *   exponentials of s = q . k / sqrt(d)                     (Eq. 4, fp32)
  * K >= M selects every team with c = 1 (dense attention).  The heads of a GQA
- * group read the union of their teams once (Appendix D).
+ * group read the union of their teams once (Appendix D); a row of a team that
+ * several heads chose is loaded once and weighed per head.
  *
  *   q         [B, Hq, d]; k_cache, v_cache token-major, for the suffix rows;
  *   seq_lens  [B] int32 device: prompt + generated rows (below N counts as N)
@@ -426,8 +426,9 @@ santa_status santa_pp_workspace_size(const santa_shape* shape, int32_t N, int32_
  *   teams     [B, Hq, K + 1] int32: the selected teams in ascending order, then
  *             the threshold team (-1 entries past min(K, M) and for K >= M)
  *   corr      [B, Hq, K] fp32: c_t of teams[j] (1 for K >= M)
- * Workspace: santa_pp_workspace_size bytes, 256-byte aligned.  Three launches
- * on stream: routing, selection (with the group's read plan) and attention.
+ * Workspace: santa_pp_workspace_size bytes, 256-byte aligned.  Four launches
+ * on stream (routing, selection, attention over the group's union, merge);
+ * calls that share a workspace must not overlap.
  */
 santa_status santa_pp_decode(const santa_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* seq_lens, int32_t N, int32_t P, int32_t R, const santa_pp_table* table,

@@ -332,24 +332,20 @@ int64_t pp_teams(int64_t N, int64_t P, int64_t R) {
 }
 
 struct PPLayout {
-    size_t arrive, done, y, phi, plan, plan_logc, plan_n, part, total;
+    size_t y, phi, logc, mask, part, total;
 };
 
-PPLayout pp_layout(const santa_shape& s, int G, int64_t M, int64_t Keff) {
+PPLayout pp_layout(const santa_shape& s, int64_t M) {
     const int64_t Mpad = (M + 3) & ~int64_t(3);
-    const int64_t PL = std::min<int64_t>(M, (int64_t)G * Keff);
     const int64_t groups = (int64_t)s.batch * s.num_kv_heads;
     const int64_t rows = (int64_t)s.batch * s.num_q_heads;
     PPLayout L;
     size_t at = 0;
     auto take = [&](size_t bytes) { const size_t r = at; at = align256(at + bytes); return r; };
-    L.arrive = take(groups * 4);
-    L.done = take(groups * 4);
     L.y = take(rows * Mpad * 4);
     L.phi = take(rows * Mpad * 4);
-    L.plan = take(groups * PL * 4);
-    L.plan_logc = take(groups * PL * G * 4);
-    L.plan_n = take(groups * 4);
+    L.logc = take(rows * Mpad * 4);
+    L.mask = take(groups * Mpad);
     L.part = take(rows * santa::kPPChunks * (int64_t)(s.head_dim + 2) * 4);
     L.total = at;
     return L;
@@ -723,7 +719,7 @@ santa_status santa_pp_workspace_size(const santa_shape* shape, int32_t N, int32_
     if (st != SANTA_STATUS_OK) return st;
     if (K < 1) return fail(SANTA_STATUS_INVALID_ARGUMENT, "the team count K must be >= 1 (got %d)", K);
     if (!bytes) return fail(SANTA_STATUS_INVALID_ARGUMENT, "bytes is NULL");
-    *bytes = pp_layout(*shape, G, M, std::min<int64_t>(K, M)).total;
+    *bytes = pp_layout(*shape, M).total;
     g_error[0] = '\0';
     return SANTA_STATUS_OK;
 }
@@ -746,7 +742,7 @@ santa_status santa_pp_decode(const santa_shape* shape, const void* q, const void
     st = pp_table_check(table);
     if (st != SANTA_STATUS_OK) return st;
     const int64_t Keff = std::min<int64_t>(K, M);
-    const PPLayout L = pp_layout(*shape, G, M, Keff);
+    const PPLayout L = pp_layout(*shape, M);
     if (workspace_bytes < L.total)
         return fail(SANTA_STATUS_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
     santa::PPParams p;
@@ -759,17 +755,13 @@ santa_status santa_pp_decode(const santa_shape* shape, const void* q, const void
     p.seed = seed;
     p.K = K;
     p.Keff = (int)Keff;
-    p.PL = (int)std::min<int64_t>(M, (int64_t)G * Keff);
     p.o = o;
     p.teams = teams;
     p.corr = corr;
-    p.arrive = reinterpret_cast<unsigned int*>(w + L.arrive);
-    p.done = reinterpret_cast<unsigned int*>(w + L.done);
     p.y = reinterpret_cast<float*>(w + L.y);
     p.phi = reinterpret_cast<float*>(w + L.phi);
-    p.plan = reinterpret_cast<int32_t*>(w + L.plan);
-    p.plan_logc = reinterpret_cast<float*>(w + L.plan_logc);
-    p.plan_n = reinterpret_cast<int32_t*>(w + L.plan_n);
+    p.logc = reinterpret_cast<float*>(w + L.logc);
+    p.mask = reinterpret_cast<unsigned int*>(w + L.mask);
     p.part = reinterpret_cast<float*>(w + L.part);
     st = hip_check(santa::launch_pp_decode(p, shape->dtype, static_cast<hipStream_t>(stream)),
                    "launching the SANTA++ decode");

@@ -7,11 +7,11 @@ namespace santa {
 
 constexpr int kPPMaxParent = 64;        // one wave per parent
 constexpr int kPPMaxTeams = 131072;     // the selection's union mask is one LDS byte per team
-constexpr int kPPChunks = 16;           // attend workgroups per (sequence, KV head)
+constexpr int kPPChunks = 32;           // attend workgroups per (sequence, KV head)
 
 struct PPParams {
     int B, Hq, Hkv, G, D;
-    int N, P, R, M, Mpad, K, Keff, PL, NC;
+    int N, P, R, M, Mpad, K, Keff, NC;
     int n_max;
     const void* q;
     const void* k;                 // token-major caches (prompt rows for the build, suffix rows for decoding)
@@ -28,13 +28,10 @@ struct PPParams {
     float* o;                      // [B, Hq, D]
     int32_t* teams;                // [B, Hq, K + 1]
     float* corr;                   // [B, Hq, K]
-    unsigned int* arrive;          // [B * Hkv]
-    unsigned int* done;            // [B * Hkv]
     float* y;                      // [B, Hq, Mpad]
     float* phi;                    // [B, Hq, Mpad]
-    int32_t* plan;                 // [B, Hkv, PL]: team | heads << 24
-    float* plan_logc;              // [B, Hkv, PL, G]
-    int32_t* plan_n;               // [B, Hkv]
+    float* logc;                   // [B, Hq, Mpad]: log c_g of the head's selected teams
+    unsigned int* mask;            // [B, Hkv, Mpad / 4]: per team, a byte of the heads that chose it
     float* part;                   // [B, Hq, NC, D + 2]
 };
 

@@ -94,4 +94,54 @@ __device__ __forceinline__ uint32_t radix_kth(const float* row, int i0, int i1, 
     return prefix;
 }
 
+// The value of an order-preserving key (the inverse of score_key; -0 comes
+// back as +0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// radix_kth over keys held in registers: thread t holds keys[0 .. nvalid).
+template <int NT, int VPT>
+__device__ __forceinline__ uint32_t radix_kth_regs(const uint32_t (&keys)[VPT], int nvalid, int k,
+                                                   unsigned int* hist, int* scan, int* krem_out) {
+    static_assert(2 * NT == kSelectBins, "two bins per thread");
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, pmask = 0;
+    int krem = k;
+    constexpr int kShift[3] = {21, 10, 0};
+    constexpr int kBits[3] = {11, 11, 10};
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = kShift[pass];
+        const uint32_t dmask = (1u << kBits[pass]) - 1u;
+        for (int j = tid; j < kSelectBins; j += NT) hist[j] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < VPT; ++e)
+            if (e < nvalid && (keys[e] & pmask) == prefix) atomicAdd(&hist[(keys[e] >> shift) & dmask], 1u);
+        __syncthreads();
+        const int c_hi = (int)hist[2 * tid + 1], c_lo = (int)hist[2 * tid];
+        const int upto = block_exclusive_sum<NT>(c_hi + c_lo, scan) + c_hi + c_lo;
+        if (tid == NT - 1) scan[2 * NW] = upto;
+        __syncthreads();
+        const int suf = scan[2 * NW] - upto;
+        if (suf < krem && krem <= suf + c_hi) {
+            scan[2 * NW + 1] = 2 * tid + 1;
+            scan[2 * NW + 2] = krem - suf;
+        } else if (suf + c_hi < krem && krem <= suf + c_hi + c_lo) {
+            scan[2 * NW + 1] = 2 * tid;
+            scan[2 * NW + 2] = krem - suf - c_hi;
+        }
+        __syncthreads();
+        const uint32_t bin = (uint32_t)scan[2 * NW + 1];
+        krem = scan[2 * NW + 2];
+        prefix |= (bin & dmask) << shift;
+        pmask |= dmask << shift;
+        __syncthreads();
+    }
+    *krem_out = krem;
+    return prefix;
+}
+
 }  // namespace santa

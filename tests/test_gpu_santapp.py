@@ -123,8 +123,7 @@ def run_decode(x, shape, table, K, seed, seq_lens=None, workspace=None):
     corr = torch.full((B, Hq, K), float("nan"), dtype=torch.float32, device=dev)
     if workspace is None:
         n = santa.santa_pp_workspace_size(shape, table["N"], table["P"], table["R"], K)
-        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
-        santa.santa_workspace_init(workspace)
+        workspace = torch.full((max(n, 256),), 0x5A, dtype=torch.uint8, device=dev)     # any contents
     lens = x["seq_lens"] if seq_lens is None else seq_lens
     santa.santa_pp_decode(shape, x["q"], x["k"], x["v"], lens, table, K, seed, o, teams, corr, workspace)
     torch.cuda.synchronize()
@@ -197,7 +196,6 @@ def test_decode_small_bf16_gqa4_with_suffix(K):
     for seed in (0, 9):
         o, teams, corr, ws = run_decode(x, shape, table, K, seed)
         print(check_decode(x, table, K, seed, o, teams, corr))
-    assert torch.count_nonzero(ws[:512]) == 0         # both counter regions are back at zero
 
 
 @pytest.mark.parametrize("G,d,dtype,P,R", [(1, 64, "f32", 8, 2), (7, 128, "bf16", 16, 4), (8, 64, "bf16", 64, 8),
