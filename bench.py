@@ -45,7 +45,8 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 METRIC = "decode attention steps/sec (heads×batch) at 32k ctx; achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ["santa_fused.hip", "santa_split.h", "santa_device.h", "santa_internal.h"]
+KERNEL_SOURCES = ["santa_fused.hip", "santa_score.hip", "santa_sample.hip", "santa_split.h", "santa_device.h",
+                  "santa_internal.h"]
 ROUNDS = 20                    # timed rounds (fewer only if fewer calls are timed)
 MAX_GRAPH_CALLS = 32           # calls captured per HIP graph
 BOUNDARY_WINDOW = 1e-6
@@ -61,8 +62,9 @@ def strip_comments(text: str) -> str:
 
 
 def kernel_source_hash(read=None) -> str:
-    """Hash of the fused kernel's sources, comments left out (a comment edit
-    does not change the kernel the counters were taken on)."""
+    """Hash of the decode kernels' sources (fused, score and sample passes),
+    comments left out (a comment edit does not change the kernels the counters
+    were taken on)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         if read is None:
@@ -75,9 +77,10 @@ def kernel_source_hash(read=None) -> str:
 
 
 def counter_traffic(workload: str):
-    """HBM bytes per fused-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fused_kernel_{workload}_counters.json")
+    """HBM bytes per decode step (the dominant kernel, or the score and sample
+    passes together) from the committed rocprofv3 counter summary of the
+    workload, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
