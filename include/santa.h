@@ -81,7 +81,7 @@
 extern "C" {
 #endif
 
-#define SANTA_ABI_VERSION 3
+#define SANTA_ABI_VERSION 4
 
 typedef enum santa_status {
     SANTA_STATUS_OK = 0,
