@@ -206,7 +206,7 @@ __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, flo
 #pragma unroll
         for (int u = 0; u < UF; ++u) {
             const int feat = __builtin_amdgcn_readlane(my_feat, u);
-            raw[u] = *reinterpret_cast<const Piece*>(gbase + (int64_t)feat * row_bytes + lane_off);
+            raw[u] = load_stream(reinterpret_cast<const Piece*>(gbase + (int64_t)feat * row_bytes + lane_off));
         }
 #pragma unroll
         for (int u = 0; u < UF; ++u) {

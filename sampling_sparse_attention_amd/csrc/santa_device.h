@@ -301,4 +301,21 @@ struct F32 {
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Loads of data that one call reads once, in a stream (the keys, a stash
+// slice): the nontemporal hint keeps these lines from displacing, in the L2
+// caches, the lines the call reads again (records, shared value rows, code).
+typedef unsigned int stream_u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int stream_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint16_t load_stream(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint32_t load_stream(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+    const stream_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const stream_u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    const stream_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const stream_u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load16_stream(const void* p) { return load_stream(reinterpret_cast<const uint4*>(p)); }
+
 }  // namespace santa

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void pp_route_kernel(PPParams p) {
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int t = t_base + it * 4 * RPW + wave * RPW + rsub;
-        kd[it] = load16(rk + (int64_t)(t < t_end ? t : t_base) * D * E::bytes);
+        kd[it] = load16_stream(rk + (int64_t)(t < t_end ? t : t_base) * D * E::bytes);
     }
     const int32_t* ts = p.team_start + (int64_t)bg * (p.M + 1);
     // this block's words of the group's selection mask start the call at zero
@@ -539,8 +539,8 @@ __global__ __launch_bounds__(256) void pp_attend_kernel(PPParams p) {
                 }
                 ei[u] = r < total ? lo : -1;
                 const int64_t row = s_first[lo] + (rr - s_pref[lo]);
-                kv[u] = load16(pk + row * D * E::bytes);
-                vv[u] = load16(pv + row * D * E::bytes);
+                kv[u] = load16_stream(pk + row * D * E::bytes);
+                vv[u] = load16_stream(pv + row * D * E::bytes);
             }
 #pragma unroll
             for (int u = 0; u < UL; ++u)
@@ -561,8 +561,8 @@ __global__ __launch_bounds__(256) void pp_attend_kernel(PPParams p) {
             for (int u = 0; u < UL; ++u) {
                 const int i = i0 + u * NG < s1 ? i0 + u * NG : s0;
                 const int64_t off = pp_row(p, b, g, i) * E::bytes;
-                kv[u] = load16(kc + off);
-                vv[u] = load16(vc + off);
+                kv[u] = load16_stream(kc + off);
+                vv[u] = load16_stream(vc + off);
             }
 #pragma unroll
             for (int u = 0; u < UL; ++u)

@@ -32,17 +32,35 @@ void sample_kernel(Params p) {
         s_err = err0;
     }
     load_pages<NT>(p, it, pages);
-    // the split's stash slice, which no other workgroup reads, is returned to
-    // zero as it is read: the workspace may next serve a problem of another
-    // layout, whose records, counts and slots can lie in these bytes and must
-    // read zero
-    for (int i = threadIdx.x; i < G * p.split; i += NT) {
-        const int h = i / p.split;
-        const int k = i - h * p.split;
-        if (k < it.ns) {
-            float* src = p.stash + ((int64_t)it.b * p.Hq + it.g * G + h) * p.stash_row + it.key0 + k;
-            sc[i] = *src;
-            *src = 0.0f;
+    // the split's stash slice in 16-byte pieces, all loads issued before any
+    // store; a piece that starts below ns may reach past it, but stays inside
+    // the stash row (T * split scores).  The slice, which no other workgroup
+    // reads, is returned to zero as it is read: the workspace may next serve a
+    // problem of another layout, whose records, counts and slots can lie in
+    // these bytes and must read zero
+    {
+        constexpr int MAXP = (G * (kMaxSplit / 4) + NT - 1) / NT;     // pieces per thread
+        const int q4 = p.split / 4;
+        uint4 v[MAXP];
+        float4* src[MAXP];
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int i = threadIdx.x + k * NT;
+            const int h = i / q4;
+            const int c = (i - h * q4) * 4;
+            src[k] = (h < G && c < it.ns)
+                         ? reinterpret_cast<float4*>(p.stash + ((int64_t)it.b * p.Hq + it.g * G + h) * p.stash_row +
+                                                     it.key0 + c)
+                         : nullptr;
+            if (src[k]) v[k] = load_stream(reinterpret_cast<const uint4*>(src[k]));
+        }
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            if (src[k]) {
+                const int i = threadIdx.x + k * NT;
+                reinterpret_cast<uint4*>(sc)[i] = v[k];
+                *src[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
         }
     }
     __syncthreads();

@@ -206,7 +206,7 @@ struct ScoreStream {
                 const int rr = r * RPL + c;
                 const bool ok = ch < nchunks && r0 + rr < it.ns;
                 const int64_t o = ok ? off + (int64_t)rr * p.stride_tok : first;
-                kd[k][r] = load16(kbase + o * E::bytes + li * 16);
+                kd[k][r] = load16_stream(kbase + o * E::bytes + li * 16);
             }
         }
     }
