@@ -337,9 +337,11 @@ typedef struct santa_kt_layout {
  * features with count_i > 0 are read from K^T, so skipped features cost no
  * bytes; feature_counts [B, Hkv, d] (uint8, device) receives count_i.
  * Arithmetic of s_hat: the weights (max m / B) count_i / m_i q_{h,i} are
- * formed in fp64 and rounded once to fp32, and each score is the sum of its
- * kept features' terms by fp32 fused multiply-adds in ascending feature
- * order, then multiplied by the fp32 1/sqrt(d).
+ * formed in fp64 and rounded once to fp32; the kept features, in ascending
+ * order, are dealt round-robin to F groups (F = 1, 2 or 4, fixed by the
+ * element size and the split), each group sums its terms by fp32 fused
+ * multiply-adds in that order, the group sums are added pairwise, and the
+ * result is multiplied by the fp32 1/sqrt(d).
  *
  *   shape        sizes and the layout of v_cache (contiguous: page_size 0)
  *   k_t, kt      K transposed and its layout (santa_kt_layout)

@@ -137,11 +137,20 @@ __device__ __forceinline__ void unpack_piece(const P& v, float (&x)[KPL]) {
         } else if constexpr (KPL == 2) {
             x[0] = __uint_as_float(v << 16);
             x[1] = __uint_as_float(v & 0xFFFF0000u);
+        } else if constexpr (KPL == 4) {
+            x[0] = __uint_as_float(v.x << 16);
+            x[1] = __uint_as_float(v.x & 0xFFFF0000u);
+            x[2] = __uint_as_float(v.y << 16);
+            x[3] = __uint_as_float(v.y & 0xFFFF0000u);
         } else {
             x[0] = __uint_as_float(v.x << 16);
             x[1] = __uint_as_float(v.x & 0xFFFF0000u);
             x[2] = __uint_as_float(v.y << 16);
             x[3] = __uint_as_float(v.y & 0xFFFF0000u);
+            x[4] = __uint_as_float(v.z << 16);
+            x[5] = __uint_as_float(v.z & 0xFFFF0000u);
+            x[6] = __uint_as_float(v.w << 16);
+            x[7] = __uint_as_float(v.w & 0xFFFF0000u);
         }
     } else {
         if constexpr (KPL == 1) {
@@ -230,10 +239,123 @@ __device__ __forceinline__ void bern_stream(const Params& p, const Item& it, flo
     priority_tail();
 }
 
-// Keys per lane of a split: a wave covers split / 4 of them, 64 lanes.
-inline int bern_kpl(int split) {
+// Estimated scores of the split's keys, whole feature rows at a time, for
+// splits of KB * 64 * PK keys (PK = 16 / element bytes keys per lane, KB in
+// {1, 2, 4}).  One 16-byte load per lane reads PK keys of a feature row, one
+// wave-wide load 64 * PK keys; wave w reads key block w mod KB of the kept
+// features f = w / KB + j * F (F = NW / KB feature groups), so every wave
+// streams its own features over its own keys with full 16-byte loads.  Feature
+// index and weights come from one lane into scalar registers, as above, and
+// the loads carry no branches (padding repeats the last kept feature with
+// weight 0; a lane past the split's keys re-reads the split's first piece; a
+// piece that the sequence ends inside is read whole, within the row).  Each
+// group's sum is the fp32 fused multiply-add sum of its features in ascending
+// order; the F group sums of a key are then added pairwise ((g0 + g1) + (g2 +
+// g3)) through LDS, before the scale.
+template <int G, typename E, int NT>
+__device__ __forceinline__ void bern_stream_rows(const Params& p, const Item& it, float* sc, float* part,
+                                                 const BernFeatures<G>& bf) {
+    constexpr int NW = NT / 64;
+    constexpr int PK = 16 / E::bytes;                          // keys per lane
+    constexpr int WK = 64 * PK;                                // keys per wave-wide load
+    constexpr int UF = G <= 4 ? 16 : 8;                        // features in flight
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int KB = p.split / WK;                               // 1, 2 or 4
+    const int F = NW / KB;
+    const int kb = wave % KB, fg = wave / KB;
+    const int lk = kb * WK + lane * PK;                        // first local key of this lane
+    const bool active = lk < it.ns;
+    const char* gbase = reinterpret_cast<const char*>(p.kt) +
+                        ((int64_t)it.b * p.kt_stride_seq + (int64_t)it.g * p.kt_stride_head + it.key0) * E::bytes;
+    const int lane_off = (active ? lk : 0) * E::bytes;        // the split's first piece is in the row
+    const int64_t row_bytes = p.kt_stride_feat * E::bytes;
+    float acc[G][PK];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < PK; ++j) acc[h][j] = 0.0f;
+    const int nf = bf.n;
+    for (int f0 = fg; f0 < nf; f0 += UF * F) {
+        // lane u < UF holds the index and weights of feature f0 + u * F
+        const int fi = f0 + lane * F;
+        const bool real = lane < UF && fi < nf;
+        const int fl = real ? fi : nf - 1;
+        const int my_feat = bf.feat[fl];
+        float my_w[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) my_w[h] = real ? bf.w[h][fl] : 0.0f;
+        uint4 raw[UF];
+#pragma unroll
+        for (int u = 0; u < UF; ++u) {
+            const int feat = __builtin_amdgcn_readlane(my_feat, u);
+            raw[u] = load16_stream(gbase + (int64_t)feat * row_bytes + lane_off);
+        }
+#pragma unroll
+        for (int u = 0; u < UF; ++u) {
+            float x[PK];
+            unpack_piece<E, PK>(raw[u], x);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w[h]), u));
+#pragma unroll
+                for (int j = 0; j < PK; ++j) acc[h][j] = fmaf(wt, x[j], acc[h][j]);
+            }
+        }
+    }
+    priority_tail();
+    // group sums to LDS: part[(fg * G + h) * split + key]
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float4* dst = reinterpret_cast<float4*>(part + (fg * G + h) * p.split + lk);
+#pragma unroll
+        for (int j = 0; j < PK; j += 4) dst[j / 4] = make_float4(acc[h][j], acc[h][j + 1], acc[h][j + 2], acc[h][j + 3]);
+    }
+    __syncthreads();
+    // pairwise sums of the F groups, (h, key) values spread over the workgroup
+    constexpr int MAXV = G * 1024 / NT;
+    const int nv = G * p.split;
+    float v[MAXV];
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+        const int i = threadIdx.x + k * NT;
+        float s = 0.0f;
+        if (i < nv) {
+            const int st = nv;                                 // stride between groups
+            if (F == 4) s = (part[i] + part[i + st]) + (part[i + 2 * st] + part[i + 3 * st]);
+            else if (F == 2) s = part[i] + part[i + st];
+            else s = part[i];
+        }
+        v[k] = s * p.scale;
+    }
+    __syncthreads();        // sc may overlap the group sums
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+        const int i = threadIdx.x + k * NT;
+        if (i < nv) {
+            const int h = i / p.split, key = i - h * p.split;
+            if (key < it.ns) sc[i] = v[k];
+        }
+    }
+}
+
+// Keys per lane of a split: a wave covers split / 4 of them, 64 lanes; 0 for
+// the whole-row stream (bern_stream_rows) where the split is 1, 2 or 4 times
+// the keys of a wave-wide 16-byte load.
+inline int bern_kpl(int split, int elem_bytes) {
+    const int wk = 64 * 16 / elem_bytes;
+    if (split >= wk && (split / wk == 1 || split / wk == 2 || split / wk == 4)) return 0;
     const int per_lane = split / (kThreads / 64) / 64;
     return per_lane >= 4 ? 4 : per_lane >= 2 ? 2 : 1;
+}
+
+// LDS of a Bernoulli workgroup: the split layout, or, if larger, the group
+// sums of the whole-row stream (F * G * split = NW * 64 * PK * G floats),
+// which overlap the layout during the stream.
+inline size_t bern_lds_bytes(const Params& p, int elem_bytes) {
+    const size_t base = split_lds_bytes(p.G, p.D, p.split, kThreads);
+    if (bern_kpl(p.split, elem_bytes) != 0) return base;
+    const size_t rows = (size_t)(kThreads / 64) * 64 * (16 / elem_bytes) * p.G * sizeof(float);
+    return rows > base ? rows : base;
 }
 
 template <int G, int D, typename E, int NT, int KPL>
@@ -249,8 +371,10 @@ void bern_fused_kernel(Params p) {
     // splits with keys need the feature list; the first split of every group,
     // keys or not, writes the counts
     if (it.ns > 0 || it.t == 0) bern_prologue<G, E, NT>(p, it, bf);
-    fused_item<G, D, E, NT>(p, it, err0, smem,
-                            [&](const Item& at, float* sc, const int*) { bern_stream<G, E, NT, KPL>(p, at, sc, bf); });
+    fused_item<G, D, E, NT>(p, it, err0, smem, [&](const Item& at, float* sc, const int*) {
+        if constexpr (KPL == 0) bern_stream_rows<G, E, NT>(p, at, sc, reinterpret_cast<float*>(smem), bf);
+        else bern_stream<G, E, NT, KPL>(p, at, sc, bf);
+    });
 }
 
 template <int G, int D, typename E, int NT, int KPL>
@@ -264,7 +388,8 @@ __global__ __launch_bounds__(NT) void bern_score_kernel(Params p) {
     const LdsLayout L = lds_layout(G, D, p.split, NT);
     float* sc = reinterpret_cast<float*>(smem + L.scratch);
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
-    bern_stream<G, E, NT, KPL>(p, it, sc, bf);
+    if constexpr (KPL == 0) bern_stream_rows<G, E, NT>(p, it, sc, reinterpret_cast<float*>(smem), bf);
+    else bern_stream<G, E, NT, KPL>(p, it, sc, bf);
     __syncthreads();
     split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     __syncthreads();
@@ -279,7 +404,8 @@ static const void* bern_fn(bool fused) {
 
 template <int G, int D, typename E>
 static const void* bern_fn_k(int kpl, bool fused) {
-    return kpl == 4 ? bern_fn<G, D, E, 4>(fused) : kpl == 2 ? bern_fn<G, D, E, 2>(fused) : bern_fn<G, D, E, 1>(fused);
+    return kpl == 0 ? bern_fn<G, D, E, 0>(fused)
+         : kpl == 4 ? bern_fn<G, D, E, 4>(fused) : kpl == 2 ? bern_fn<G, D, E, 2>(fused) : bern_fn<G, D, E, 1>(fused);
 }
 
 template <int D, typename E>
@@ -295,7 +421,7 @@ static const void* bern_fn_g(int G, int kpl, bool fused) {
 }
 
 static const void* bern_function(const Params& p, int dtype, bool fused) {
-    const int kpl = bern_kpl(p.split);
+    const int kpl = bern_kpl(p.split, dtype == 0 ? 2 : 4);
     if (dtype == 0) return p.D == 64 ? bern_fn_g<64, Bf16>(p.G, kpl, fused) : bern_fn_g<128, Bf16>(p.G, kpl, fused);
     return p.D == 64 ? bern_fn_g<64, F32>(p.G, kpl, fused) : bern_fn_g<128, F32>(p.G, kpl, fused);
 }
@@ -303,7 +429,7 @@ static const void* bern_function(const Params& p, int dtype, bool fused) {
 static hipError_t launch_bern(const Params& p, int dtype, hipStream_t stream, bool fused) {
     const void* fn = bern_function(p, dtype, fused);
     if (!fn) return hipErrorInvalidValue;
-    const size_t lds = split_lds_bytes(p.G, p.D, p.split, kThreads);
+    const size_t lds = bern_lds_bytes(p, dtype == 0 ? 2 : 4);
     const hipError_t e = allow_lds(fn, lds);
     if (e != hipSuccess) return e;
     void* args[] = {const_cast<Params*>(&p)};
@@ -316,7 +442,7 @@ hipError_t launch_bern_score(const Params& p, int dtype, hipStream_t stream) { r
 int bern_fused_blocks_per_cu(const Params& p, int dtype) {
     const void* fn = bern_function(p, dtype, true);
     if (!fn) return 0;
-    const size_t lds = split_lds_bytes(p.G, p.D, p.split, kThreads);
+    const size_t lds = bern_lds_bytes(p, dtype == 0 ? 2 : 4);
     if (allow_lds(fn, lds) != hipSuccess) return 0;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, lds) != hipSuccess) return 0;

@@ -7,10 +7,10 @@ against oracle/bernoulli.py through the C ABI.
   estimated scores, except for targets within a CDF window of an interval
   edge.  The window is 1e-6 (the exact path's) plus twice the p-weighted bound
   on the GPU's fp32 score error.  The library states its summation: the
-  weights are rounded once to fp32 and each score sums its kept features'
-  terms by fused multiply-adds in ascending feature order.  The bound below
-  also covers the same sum split round-robin over F lane groups whose sums are
-  added pairwise (F a power of two up to 32; F = 1 is the sequential sum): to
+  weights are rounded once to fp32, the kept features (ascending) are dealt
+  round-robin to F groups, each group sums its terms by fused multiply-adds in
+  order and the group sums are added pairwise.  The bound below covers every
+  such split (F a power of two up to 32; F = 1 is the sequential sum): to
   first order the error of key j's score is at most 2^-24 times (the sum of
   |w_f k_jf| for the weights' rounding, plus the magnitudes of every group's
   running sums, plus log2(F) times the sum of |w_f k_jf| for the pairwise
