@@ -6,7 +6,9 @@
 // "Stratified Sparse Attention" page does: the k-th largest score is found
 // digit by digit from histograms, without sorting the row.
 //
-// One workgroup per (sequence, query head):
+// One workgroup per (sequence, query head).  A row of at most kTopkThreads *
+// kTopkRegs scores is read once into registers (and its stash returned to
+// zero then); a longer one is read from the stash in every pass below.
 //   1. the row maximum M (for the weights exp(s - M));
 //   2. three radix passes over order-preserving 32-bit keys of the scores
 //      (11, 11 and 10 bits): each counts, among the keys that match the digits
@@ -26,6 +28,7 @@ namespace santa {
 constexpr int kTopkThreads = kSelectBins / 2;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kTopkBins = kSelectBins;
+constexpr int kTopkRegs = 32;           // scores per thread held in registers
 
 // Element offset of V row `key` of KV head g of sequence b.
 __device__ __forceinline__ int64_t v_row(const Params& p, int b, int g, int key) {
@@ -66,15 +69,38 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params p) {
     // thread t owns keys [i0, i1): a multiple of 4 keys, so its reads are 16-byte aligned
     const int C = ((n + kTopkThreads - 1) / kTopkThreads + 3) & ~3;
     const int i0 = min(n, tid * C), i1 = min(n, i0 + C);
+    const bool regs = C <= kTopkRegs;       // the same in every thread
+    float sr[kTopkRegs];
+    uint32_t kr[kTopkRegs];
+    if (regs) {
+#pragma unroll
+        for (int c = 0; c < kTopkRegs; c += 4) {
+            float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (i0 + c < i1) {
+                float4* src = reinterpret_cast<float4*>(row + i0 + c);
+                v = *src;
+                *src = make_float4(0.0f, 0.0f, 0.0f, 0.0f);      // the stash returns to zero
+            }
+            sr[c] = v.x; sr[c + 1] = v.y; sr[c + 2] = v.z; sr[c + 3] = v.w;
+        }
+#pragma unroll
+        for (int c = 0; c < kTopkRegs; ++c) kr[c] = score_key(sr[c]);
+    }
 
     // 1. the maximum score
     float mx = -INFINITY;
-    for (int i = i0; i < i1; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + i);
-        mx = fmaxf(mx, v.x);
-        if (i + 1 < i1) mx = fmaxf(mx, v.y);
-        if (i + 2 < i1) mx = fmaxf(mx, v.z);
-        if (i + 3 < i1) mx = fmaxf(mx, v.w);
+    if (regs) {
+#pragma unroll
+        for (int c = 0; c < kTopkRegs; ++c)
+            if (i0 + c < i1) mx = fmaxf(mx, sr[c]);
+    } else {
+        for (int i = i0; i < i1; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + i);
+            mx = fmaxf(mx, v.x);
+            if (i + 1 < i1) mx = fmaxf(mx, v.y);
+            if (i + 2 < i1) mx = fmaxf(mx, v.z);
+            if (i + 3 < i1) mx = fmaxf(mx, v.w);
+        }
     }
     mx = wave_max_f32(mx);
     if (lane == 0) reinterpret_cast<float*>(scan)[wave] = mx;
@@ -85,21 +111,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params p) {
 
     // 2. radix passes: the k-th largest key, digit by digit from the top
     int krem = 0;
-    const uint32_t prefix = radix_kth<kTopkThreads>(row, i0, i1, k, hist, scan, &krem);
+    const uint32_t prefix = regs ? radix_kth_regs<kTopkThreads, kTopkRegs>(kr, i1 - i0, k, hist, scan, &krem)
+                                 : radix_kth<kTopkThreads>(row, i0, i1, k, hist, scan, &krem);
     // prefix is the k-th largest key; krem keys equal to it are kept (the lowest indices)
     const uint32_t kth = prefix;
 
     // 3. selection in index order
     int n_eq = 0, n_gt = 0;
-    for (int i = i0; i < i1; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + i);
-        const float sv[4] = {v.x, v.y, v.z, v.w};
+    if (regs) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t key = score_key(sv[e]);
-            if (i + e < i1) {
-                n_gt += key > kth ? 1 : 0;
-                n_eq += key == kth ? 1 : 0;
+        for (int c = 0; c < kTopkRegs; ++c) {
+            if (i0 + c < i1) {
+                n_gt += kr[c] > kth ? 1 : 0;
+                n_eq += kr[c] == kth ? 1 : 0;
+            }
+        }
+    } else {
+        for (int i = i0; i < i1; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(row + i);
+            const float sv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t key = score_key(sv[e]);
+                if (i + e < i1) {
+                    n_gt += key > kth ? 1 : 0;
+                    n_eq += key == kth ? 1 : 0;
+                }
             }
         }
     }
@@ -108,28 +145,34 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(Params p) {
     int pos = block_exclusive_sum<kTopkThreads>(n_gt + take_eq, scan);
     float wsum = 0.0f;
     int eq_seen = 0;
-    for (int i = i0; i < i1; i += 4) {
-        float4* src = reinterpret_cast<float4*>(row + i);
-        const float4 v = *src;
-        *src = make_float4(0.0f, 0.0f, 0.0f, 0.0f);      // the stash returns to zero
-        const float sv[4] = {v.x, v.y, v.z, v.w};
+    auto consider = [&](int i, float s, uint32_t key) {
+        bool keep = key > kth;
+        if (key == kth) {
+            keep = eq_seen < take_eq;
+            ++eq_seen;
+        }
+        if (keep && pos < k) {          // exactly k are kept; the bound only guards the writes
+            const float w = __expf(s - M);
+            idx[pos] = i;
+            kept_i[pos] = i;
+            kept_w[pos] = w;
+            wsum += w;
+            ++pos;
+        }
+    };
+    if (regs) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (i + e >= i1) continue;
-            const uint32_t key = score_key(sv[e]);
-            bool keep = key > kth;
-            if (key == kth) {
-                keep = eq_seen < take_eq;
-                ++eq_seen;
-            }
-            if (keep && pos < k) {          // exactly k are kept; the bound only guards the writes
-                const float w = __expf(sv[e] - M);
-                idx[pos] = i + e;
-                kept_i[pos] = i + e;
-                kept_w[pos] = w;
-                wsum += w;
-                ++pos;
-            }
+        for (int c = 0; c < kTopkRegs; ++c)
+            if (i0 + c < i1) consider(i0 + c, sr[c], kr[c]);
+    } else {
+        for (int i = i0; i < i1; i += 4) {
+            float4* src = reinterpret_cast<float4*>(row + i);
+            const float4 v = *src;
+            *src = make_float4(0.0f, 0.0f, 0.0f, 0.0f);      // the stash returns to zero
+            const float sv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (i + e < i1) consider(i + e, sv[e], score_key(sv[e]));
         }
     }
     // the sum of the kept weights
