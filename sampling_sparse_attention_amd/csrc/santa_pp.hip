@@ -276,6 +276,7 @@ __device__ __forceinline__ void mark_team(unsigned int* mask, int t, unsigned in
 }
 
 constexpr int kPPRegVals = 16;      // scores per thread held in registers (M <= 16384)
+constexpr int kPPStage = 1024;      // kept teams staged in LDS before their corrections
 
 // A kept team: its slot in the output, its correction (Eq. 7, fp64), its log c
 // for the attention and its bit in the group's mask.
@@ -293,6 +294,8 @@ __global__ __launch_bounds__(kPPSelectThreads) void pp_select_kernel(PPParams p)
     constexpr int NT = kPPSelectThreads;
     __shared__ unsigned int hist[kSelectBins];
     __shared__ int scan[2 * (NT / 64) + 4];
+    __shared__ int s_team[kPPStage];
+    __shared__ float s_phi[kPPStage];
     const int bh = blockIdx.x;
     const int b = bh / p.Hq, hq = bh - b * p.Hq;
     const int g = hq / p.G, h = hq - g * p.G;
@@ -354,6 +357,7 @@ __global__ __launch_bounds__(kPPSelectThreads) void pp_select_kernel(PPParams p)
         const int has_thr = (eq_before <= krem - 1 && krem - 1 < eq_before + n_eq) ? 1 : 0;
         int pos = block_exclusive_sum<NT>(n_gt + take_eq - has_thr, scan);
         int eq_seen = 0;
+        const bool staged = Keff <= kPPStage;
 #pragma unroll
         for (int e = 0; e < kPPRegVals; ++e) {
             if (e >= nvalid) continue;
@@ -367,7 +371,21 @@ __global__ __launch_bounds__(kPPSelectThreads) void pp_select_kernel(PPParams p)
                 }
                 ++eq_seen;
             }
-            if (keep && pos < Keff) keep_team(p, teams, corr, lc, mask, bit, pos++, i0 + e, ph[e], tau);
+            if (keep && pos < Keff) {
+                if (staged) {
+                    s_team[pos] = i0 + e;
+                    s_phi[pos] = ph[e];
+                    ++pos;
+                } else {
+                    keep_team(p, teams, corr, lc, mask, bit, pos++, i0 + e, ph[e], tau);
+                }
+            }
+        }
+        if (staged) {
+            // the corrections one kept team per thread, instead of once per
+            // register slot in every wave that keeps a team there
+            __syncthreads();
+            for (int j = tid; j < Keff; j += NT) keep_team(p, teams, corr, lc, mask, bit, j, s_team[j], s_phi[j], tau);
         }
     } else {
         // long rows: the same from memory
