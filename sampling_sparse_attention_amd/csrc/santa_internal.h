@@ -45,7 +45,7 @@ constexpr int kBarrierStride = 32 * kBarrierLines;   // 32-bit words per (sequen
 // Partial outputs: each split adds its per-head sums into accumulation slot
 // (split % kOutSlots) of its (sequence, KV head), so few additions meet on one
 // word; the last split to finish sums the slots into o and clears them.
-constexpr int kOutSlots = 16;
+constexpr int kOutSlots = 8;
 
 // Orders of the work items (sequence, KV head, split) over the workgroup indices.
 constexpr int kOrderSplitFastest = 0;

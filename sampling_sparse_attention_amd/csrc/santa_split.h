@@ -1069,7 +1069,7 @@ __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& i
         st.stream = 0;
         st.off = 0;
         if (st.m_hi > st.m_lo) {
-            // into accumulation slot t mod 16 of the group
+            // into accumulation slot t mod kOutSlots of the group
             float* slot = p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D;
             sample_head<G, D, E, KW, UL>(p, it, st, h, L, smem, [&](int col, const float* vals) {
 #pragma unroll
