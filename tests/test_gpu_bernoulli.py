@@ -158,7 +158,9 @@ def test_bernoulli_sampling_modes(mode):
 @pytest.mark.parametrize("G,d,dtype", [(1, 64, "f32"), (7, 128, "bf16"), (8, 64, "bf16"), (2, 128, "f32")])
 def test_bernoulli_shapes(G, d, dtype):
     x = _inputs(G=G, d=d, dtype=dtype, lens=(3001, 700, 1, 0), seed=G)
-    for split in (0, 64, 1024):
+    # 64: a quarter of a row per wave; 256 .. 1024: whole feature rows per wave
+    # (bf16 512 / 1024 and fp32 256 / 512 / 1024 are one, two and four key blocks)
+    for split in (0, 64, 256, 512, 1024):
         o, idx, counts, _ = run_bern(x, 128, W.MODE_SYSTEMATIC, 2, 8, split=split)
         print(split, check_bern(x, 128, W.MODE_SYSTEMATIC, 2, 8, o, idx, counts))
 
