@@ -114,7 +114,9 @@ enum {
  *                                 + g * kv_stride_head,
  *                                 P = block_table[b * pages_per_seq + i / page_size]
  * and holds head_dim contiguous elements.  K and V share the layout.  Every
- * row must start on a 16-byte boundary.
+ * row must start on a 16-byte boundary.  A contiguous cache holds the rows of
+ * tokens 0 .. max_seq_len - 1 of every sequence: the score pass may read K
+ * rows past a sequence's length (their scores are never used).
  */
 typedef struct santa_shape {
     int32_t batch;            /* B >= 1 */

@@ -40,7 +40,8 @@ void flash_kernel(Params p) {
 
     load_pages<NT>(p, it, pages);
     __syncthreads();
-    stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
+    uint4 kd[ScoreStream<G, D, E, NT>::CB][ScoreStream<G, D, E, NT>::R];
+    stream_scores<G, D, E, NT>(p, it, sc, pages, qf, kd, false);
     __shared__ unsigned int s_err;      // thread 0's read, the same for the whole workgroup
     if (threadIdx.x == 0) s_err = err0;
     __syncthreads();

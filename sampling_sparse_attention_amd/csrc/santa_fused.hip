@@ -24,10 +24,13 @@ void fused_kernel(Params p) {
     uint4 qf[G];
     priority_streaming();
     load_q<G, D, E, NT>(p, at.b, at.g, qf);
+    // the first K batch in flight with q and the sequence length
+    uint4 kd[ScoreStream<G, D, E, NT>::CB][ScoreStream<G, D, E, NT>::R];
+    const bool pre = stream_first_batch<G, D, E, NT>(p, at, kd);
     const unsigned int err0 = p.sync->error;    // in flight with q, used after the K stream
     fused_item<G, D, E, NT>(p, make_item(p, item), err0, smem,
                             [&](const Item& it, float* sc, const int* pages) {
-                                stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
+                                stream_scores<G, D, E, NT>(p, it, sc, pages, qf, kd, pre);
                             });
 }
 

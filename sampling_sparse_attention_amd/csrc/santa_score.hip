@@ -30,7 +30,8 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
         HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
         load_pages<NT>(p, it, pages);
         __syncthreads();
-        stream_scores<G, D, E, NT>(p, it, sc, pages, qf);
+        uint4 kd[ScoreStream<G, D, E, NT>::CB][ScoreStream<G, D, E, NT>::R];
+        stream_scores<G, D, E, NT>(p, it, sc, pages, qf, kd, false);
         __syncthreads();
         if constexpr (STATS) {
             split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);

@@ -255,9 +255,34 @@ __device__ __forceinline__ void load_q(const Params& p, int b, int g, uint4 (&qf
     for (int h = 0; h < G; ++h) qf[h] = load16(qb + (int64_t)h * D * E::bytes);
 }
 
+// The first batch of a split's K loads in a contiguous cache, issued before
+// the sequence length is known: its rows are bounded by the cache's n_max rows
+// instead of by the sequence (every such row is inside the cache), and the
+// scores of rows past the sequence are never written.  Returns whether it
+// issued them: only in the resident fused launch (a split past its sequence
+// would read its batch for nothing, which in batches of short sequences costs
+// more than the round trip saved) and not for paged caches, whose rows need
+// the split's pages.
+template <int G, int D, typename E, int NT>
+__device__ __forceinline__ bool stream_first_batch(const Params& p, const Item& at,
+                                                   uint4 (&kd)[ScoreStream<G, D, E, NT>::CB][ScoreStream<G, D, E, NT>::R]) {
+    using SS = ScoreStream<G, D, E, NT>;
+    if (p.page_shift >= 0 || p.use_ticket) return false;
+    Item sp = at;
+    sp.key0 = at.t * p.split;
+    sp.ns = max(0, min(p.split, p.n_max - sp.key0));
+    const int lane = threadIdx.x & 63;
+    SS::template issue<SS::CB>(p, sp, nullptr, reinterpret_cast<const char*>(p.k), row_offset(p, sp, 0, nullptr),
+                               threadIdx.x >> 6, (sp.ns + 15) >> 4, lane / SS::LPR, lane % SS::LPR, kd);
+    return true;
+}
+
+// `kd`/`pre`: the first batch as stream_first_batch issued it, if it did.
 template <int G, int D, typename E, int NT>
 __device__ __forceinline__ void stream_scores(const Params& p, const Item& it, float* sc,
-                                              const int* pages, const uint4 (&qf)[G]) {
+                                              const int* pages, const uint4 (&qf)[G],
+                                              uint4 (&kd)[ScoreStream<G, D, E, NT>::CB][ScoreStream<G, D, E, NT>::R],
+                                              bool pre) {
     using SS = ScoreStream<G, D, E, NT>;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -267,8 +292,7 @@ __device__ __forceinline__ void stream_scores(const Params& p, const Item& it, f
     const int nchunks = (it.ns + 15) >> 4;
     const int64_t first = row_offset(p, it, 0, pages);
 
-    uint4 kd[SS::CB][SS::R];
-    SS::template issue<SS::CB>(p, it, pages, kbase, first, wave, nchunks, c, li, kd);
+    if (!pre) SS::template issue<SS::CB>(p, it, pages, kbase, first, wave, nchunks, c, li, kd);
     SS::template score<SS::CB>(p, it, sc, wave, nchunks, c, li, qf, kd);
     for (int base = wave + SS::NW * SS::CB; base < nchunks; base += SS::NW * SS::CB) {
         SS::template issue<SS::CB>(p, it, pages, kbase, first, base, nchunks, c, li, kd);
