@@ -238,16 +238,18 @@ def test_large_grid_repeated_calls_match_split_stages_and_oracle():
 
 def test_workspace_reused_across_calls_and_shapes():
     """Calls leave the workspace zero, so one workspace serves many calls of different shapes in a row,
-    mixing the fused kernel and the two halves."""
-    xa = _inputs(lens=(2049, 700, 1))
-    xb = _inputs(G=1, d=64, dtype="f32", lens=(300, 0, 1500))
+    mixing the fused kernel and the two halves; every call has its own q, K and V, so a record,
+    count or slot left over from an earlier call would show in the indices or the output."""
+    xs_a = [_inputs(lens=(2049, 700, 1), seed=30 + r) for r in range(3)]
+    xs_b = [_inputs(G=1, d=64, dtype="f32", lens=(300, 0, 1500), seed=40 + r) for r in range(3)]
     big = max(santa.santa_workspace_size(santa.make_shape(x["q"], x["k"], None,
                                                           max_seq_len=x["workload"].seq_len), 128, 0)
-              for x in (xa, xb))
+              for x in (xs_a[0], xs_b[0]))
     ws = torch.empty(big, dtype=torch.uint8, device="cuda")
     santa.santa_workspace_init(ws)
     for rep in range(3):
-        for x, mode in ((xa, 2), (xb, 0), (xa, 1), (xb, 2)):
+        xa, xb, xa2, xb2 = xs_a[rep], xs_b[rep], xs_a[(rep + 1) % 3], xs_b[(rep + 1) % 3]
+        for x, mode in ((xa, 2), (xb, 0), (xa2, 1), (xb2, 2)):
             shape = santa.make_shape(x["q"], x["k"], None, max_seq_len=x["workload"].seq_len)
             B, Hq, d = x["q"].shape
             o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
