@@ -65,22 +65,28 @@ __device__ __forceinline__ double mean_abs_query(const Params& p, int b, int g, 
 // fl((n + 1) / B) < pi and never when fl(n / B) >= pi; only the other draws
 // need their uniform.  With n0 = floor(B pi) (B <= 64, so 1/B dwarfs the
 // rounding) every draw below n0 - 1 is certain and every draw above n0 + 1
-// impossible: at most three draws are looked at, one or two Philox blocks.
+// impossible, so three draws are looked at; and at most one of them needs its
+// uniform (if fl(n / B) < pi <= fl((n + 1) / B), draw n + 1 is impossible and
+// draw n - 1 certain), so every lane computes at most one Philox block, all
+// lanes at once.  Dividing by a power-of-two B is a multiplication by its
+// exact reciprocal.
 __device__ __forceinline__ int bern_count(double pi, int B, uint64_t seed, int b, int g, int i) {
     if (!(pi > 0.0)) return 0;
     const double Bd = (double)B;
+    const bool pow2 = (B & (B - 1)) == 0;
+    const double invB = 1.0 / Bd;
+    auto over_b = [&](double x) { return pow2 ? x * invB : x / Bd; };
     const int n0 = min((int)floor(Bd * pi), B);
     int c = max(n0 - 1, 0);
-    const int n1 = min(n0 + 1, B - 1);
-    for (int n = max(n0 - 1, 0); n <= n1; ++n) {
-        if ((double)(n + 1) / Bd < pi) {
-            ++c;
-        } else if ((double)n / Bd >= pi) {
-            break;                                  // and so are all later draws
-        } else if (((double)n + bern_uniform(seed, b, g, i, n)) / Bd < pi) {
-            ++c;
-        }
+    int un = -1;                                    // the draw that needs its uniform, if any
+#pragma unroll
+    for (int k = -1; k <= 1; ++k) {
+        const int n = n0 + k;
+        if (n < 0 || n >= B) continue;
+        if (over_b((double)(n + 1)) < pi) ++c;
+        else if (!(over_b((double)n) >= pi)) un = n;
     }
+    if (un >= 0 && over_b((double)un + bern_uniform(seed, b, g, i, un)) < pi) ++c;
     return c;
 }
 

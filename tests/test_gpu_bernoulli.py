@@ -139,7 +139,7 @@ def check_bern(x, S, mode, seed, B, o, idx, counts, heads=None, label=None):
     return rep
 
 
-@pytest.mark.parametrize("B", [1, 8, 64])
+@pytest.mark.parametrize("B", [1, 8, 12, 64])          # 12: a B that is not a power of two
 def test_bernoulli_small_bf16_gqa4(B):
     x = _inputs(B=B)
     o, idx, counts, ws = run_bern(x, 256, W.MODE_SYSTEMATIC, 11, B)
