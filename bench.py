@@ -495,7 +495,7 @@ def pp_line(santa, steps, eager, dev, ncopies):
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import sampling_sparse_attention_amd as santa

@@ -28,14 +28,16 @@ def golden_dir():
 
 def pytest_sessionfinish(session, exitstatus):
     """Writes the boundary-case counts and worst relative L2 of every GPU parity
-    configuration checked in this session to gpurun_out/parity_report.json."""
+    configuration checked in this session to parity_report.json in the output folder
+    (PARITY_REPORT_DIR, by default the repository's output folder, whose contents a run
+    on another machine brings back)."""
     import json
     import sys
     helpers = sys.modules.get("tests.gpu_helpers")
     reports = getattr(helpers, "SESSION_REPORTS", None) if helpers else None
     if not reports:
         return
-    out = os.path.join(ROOT, "gpurun_out")
+    out = os.environ.get("PARITY_REPORT_DIR") or os.path.join(ROOT, "gpurun_out")
     os.makedirs(out, exist_ok=True)
     total = dict(configs=len(reports), heads=0, targets=0, boundary_cases=0, boundary_mismatches=0,
                  worst_rel_l2=0.0)

@@ -64,7 +64,7 @@ def oracle_head(x: dict, b: int, h: int, S: int, mode: int, seed: int, rows=None
 
 
 # Parity reports of this test session by configuration; tests/conftest.py writes
-# them to gpurun_out/parity_report.json when the session ends.
+# them to parity_report.json in the run's output folder when the session ends.
 SESSION_REPORTS = {}
 
 
