@@ -145,16 +145,21 @@ typedef struct santa_shape {
  *            counts of its splits that have published their records and that
  *            have added their output in the current call, and 16 copies of a
  *            flag raised once all of them published;
- *   accum    fp32 [B, Hkv, 16, G, d]: partial outputs, added by the splits of a
- *            (sequence, KV head) into slot (split % 16) and summed into o by
+ *   accum    fp32 [B, Hkv, 8, G, d]: partial outputs, added by the splits of a
+ *            (sequence, KV head) into slot (split % 8) and summed into o by
  *            the last of them;
  *   flash    santa_decode_flash only: per (sequence, query head) a 64-bit
  *            reference maximum, then (256-byte aligned) fp64 accumulators
- *            [B, Hkv, 16, G, d + 2] of weighted tile means and weights;
+ *            [B, Hkv, 8, G, d + 2] of weighted tile means and weights;
  *   records  [B, Hq, num_splits] x 8 bytes: per split the maximum score m and
  *            l = sum exp(s_i - m) (the tile partition functions of section 3.2,
  *            Pass 1) as one word, fp32 l in the high and fp32 m in the low half
- *            (l >= 1 for a split with keys, so 0 means not written yet);
+ *            (l >= 1 for a split with keys, so 0 means not written yet); then
+ *            [B, Hq, num_splits + 2] x 8 bytes of the two-kernel path: the
+ *            exclusive prefix W_t of the split masses (2^-40 fixed point),
+ *            the total Z after the sequence's last split, and at the end the
+ *            maximum M (fp32, low half) and the last split of positive mass
+ *            (high half), written by the last split of the score pass;
  *   stash    fp32 [B, Hq, num_splits * split_size]: scaled scores s_i (the
  *            "score stash" of section 3.2, Pass 1), written by
  *            santa_score_pass and read (and cleared) by santa_sample_pass; row

@@ -135,7 +135,8 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     L.records_offset = align256(L.flash_offset + align256(rows * sizeof(unsigned long long)) +
                                 (size_t)s->batch * s->num_q_heads * santa::kOutSlots * (s->head_dim + 2) *
                                     sizeof(double));
-    L.stash_offset = align256(L.records_offset + rows * (size_t)T * 8);
+    // split records [B, Hq, T], then the group prefixes [B, Hq, T + 2]
+    L.stash_offset = align256(L.records_offset + rows * (size_t)T * 8 + rows * (size_t)(T + 2) * 8);
     L.stash_row_bytes = (size_t)T * split * sizeof(float);
     L.targets_offset = align256(L.stash_offset + rows * L.stash_row_bytes);
     const size_t targets = mode == SANTA_MODE_MULTINOMIAL ? rows * (size_t)S * sizeof(double) : 0;
@@ -176,6 +177,7 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->idx = idx;
     p->sync = reinterpret_cast<santa::SyncWords*>(w + L.sync_offset);
     p->records = reinterpret_cast<unsigned long long*>(w + L.records_offset);
+    p->gprefix = p->records + (size_t)s->batch * s->num_q_heads * plan->T;
     p->barrier = reinterpret_cast<unsigned int*>(w + L.barrier_offset);
     p->accum = reinterpret_cast<float*>(w + L.accum_offset);
     p->flash_ref = reinterpret_cast<unsigned long long*>(w + L.flash_offset);

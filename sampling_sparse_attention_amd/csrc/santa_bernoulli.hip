@@ -400,6 +400,7 @@ __global__ __launch_bounds__(NT) void bern_score_kernel(Params p) {
     split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
     __syncthreads();
     write_stash<G, NT>(p, it, sc);
+    publish_group_prefix<G, NT>(p, it);
 }
 
 template <int G, int D, typename E, int KPL>

@@ -62,6 +62,7 @@ struct Params {
     int32_t* idx;
     SyncWords* sync;
     unsigned long long* records;  // [B, Hq, T] words: l bits << 32 | m bits (0: not written yet)
+    unsigned long long* gprefix;  // two-kernel path: [B * Hq][T + 2] split-mass prefixes W_t, Z, then M | last << 32
     unsigned int* barrier;        // [B * Hkv] x kBarrierStride words: counts, flags
     float* accum;                 // [B * Hkv][kOutSlots][G * D] partial outputs (zero between calls)
     double* flash_acc;            // S^2ANTA-flash: [B * Hkv][kOutSlots][G][D + 2] weighted sums, weight

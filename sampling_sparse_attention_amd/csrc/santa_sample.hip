@@ -71,10 +71,11 @@ void sample_kernel(Params p) {
         if (it.t == 0) poison_group<G, D, NT>(p, it);
         return;
     }
-    // the records come from the score pass, an earlier launch: one missing now
-    // means no score pass preceded this one, which is an error, not a wait
-    prefix_and_sample<G, D, E, NT>(p, it, L, smem, 0, &s_fail);
-    finish_output<G, D, NT>(p, it, &s_fail);
+    // the group's prefix comes from the score pass's last split (an earlier
+    // launch): one missing now means no score pass preceded this one, which is
+    // an error, not a wait
+    prefix_and_sample<G, D, E, NT, true>(p, it, L, smem, 0, &s_fail);
+    finish_output<G, D, NT>(p, it, &s_fail, true);
 }
 
 template <int G, int D, typename E>

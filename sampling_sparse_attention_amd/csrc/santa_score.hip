@@ -38,6 +38,7 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
             __syncthreads();
         }
         write_stash<G, NT>(p, it, sc);
+        if constexpr (STATS) publish_group_prefix<G, NT>(p, it);
     }
 }
 

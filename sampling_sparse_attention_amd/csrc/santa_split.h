@@ -970,6 +970,98 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
 }
 
 // ---------------------------------------------------------------------------
+// The Tb split records of one query head, K = 2^record_shift per lane (lane L
+// holds records L*K .. L*K + K - 1): first an ordinary (cached) read -- once
+// every split has counted itself in, the records are normally in place, and
+// the splits' workgroups on one XCD then share its L2 copy -- then, for any
+// not written yet, device-coherent re-reads until they are.  Returns false
+// (and sets the error word and *fail) after `spin_limit` re-reads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool read_records(const Params& p, const unsigned long long* rec, int Tb, int K,
+                                             int spin_limit, float (&mr)[kRecPerLane], float (&lr)[kRecPerLane],
+                                             int* fail) {
+    const int lane = threadIdx.x & 63;
+    bool fresh = true;
+#pragma unroll
+    for (int k = 0; k < kRecPerLane; ++k) {
+        const int j = lane * K + k;
+        mr[k] = -INFINITY;
+        lr[k] = 0.0f;
+        if (k < K && j < Tb) {
+            const unsigned long long r = rec[j];
+            fresh &= (r >> 32) != 0;
+            mr[k] = __uint_as_float((uint32_t)r);
+            lr[k] = __uint_as_float((uint32_t)(r >> 32));
+        }
+    }
+    for (int iter = 0; !__all(fresh); ++iter) {
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < kRecPerLane; ++k) {
+            const int j = lane * K + k;
+            mr[k] = -INFINITY;
+            lr[k] = 0.0f;
+            if (k < K && j < Tb) {
+                const unsigned long long r = __hip_atomic_load(rec + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok &= (r >> 32) != 0;
+                mr[k] = __uint_as_float((uint32_t)r);
+                lr[k] = __uint_as_float((uint32_t)(r >> 32));
+            }
+        }
+        if (__all(ok)) break;
+        if (iter >= spin_limit) {
+            if (lane == 0) {
+                __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *fail = 1;
+            }
+            return false;       // the same in every lane of the wave
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
+// The split masses w_j = l_j * exp(m_j - M) of one head as 2^-40 fixed point
+// and their exact prefix: M, the total Z, the last split of positive mass,
+// this lane's exclusive prefix `excl` and, per record k of the lane, the sum
+// of the lane's records before it.
+struct GroupPrefix {
+    float M;
+    uint64_t Z, excl;
+    int last;
+    uint64_t before[kRecPerLane];
+};
+
+__device__ __forceinline__ GroupPrefix group_prefix(const float (&mr)[kRecPerLane], const float (&lr)[kRecPerLane],
+                                                    int Tb, int K) {
+    const int lane = threadIdx.x & 63;
+    GroupPrefix g;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kRecPerLane; ++k) mx = fmaxf(mx, mr[k]);
+    g.M = wave_max_f32(mx);
+    uint64_t run = 0;
+    int last = -1;
+#pragma unroll
+    for (int k = 0; k < kRecPerLane; ++k) {
+        const int j = lane * K + k;
+        uint64_t w = 0;
+        if (k < K && j < Tb) {
+            const double f = (double)mass_exp(mr[k] - g.M);
+            w = fixed40((double)lr[k] * f);
+            if (w) last = j;
+        }
+        g.before[k] = run;
+        run += w;
+    }
+    const uint64_t incl = wave_scan_add_u64(run);
+    g.excl = incl - run;
+    g.Z = lane_u64(incl, 63);
+    g.last = wave_max_i32(last);
+    return g;
+}
+
+// ---------------------------------------------------------------------------
 // Global partition function, this split's target range, then the head's
 // sampling and gather (one wave per head, no workgroup barrier).
 // Split masses w_j = l_j * exp(m_j - M) are summed as fixed point with 2^-40
@@ -980,7 +1072,7 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
 // and the head is skipped: nothing is computed from an incomplete set of
 // records.
 // ---------------------------------------------------------------------------
-template <int G, int D, typename E, int NT, int KW = 4, int UL = 8>
+template <int G, int D, typename E, int NT, bool FROM_PREFIX = false, int KW = 4, int UL = 8>
 __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
                                                   unsigned char* smem, int spin_limit, int* fail) {
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
@@ -993,85 +1085,45 @@ __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& i
     const int K = 1 << ks;
     for (int h = wave; h < G; h += NW) {
         const int hq = it.g * G + h;
-        const unsigned long long* rec = record_of(p, it.b, hq, 0);
-        float mr[kRecPerLane], lr[kRecPerLane];
-        // first an ordinary (cached) read: after the barrier every record is
-        // normally in place, and the splits' workgroups on one XCD then share
-        // its L2 copy; a record not written yet is re-read below with
-        // device-coherent loads until it is
-        bool fresh = true;
-#pragma unroll
-        for (int k = 0; k < kRecPerLane; ++k) {
-            const int j = lane * K + k;
-            mr[k] = -INFINITY;
-            lr[k] = 0.0f;
-            if (k < K && j < Tb) {
-                const unsigned long long r = rec[j];
-                fresh &= (r >> 32) != 0;
-                mr[k] = __uint_as_float((uint32_t)r);
-                lr[k] = __uint_as_float((uint32_t)(r >> 32));
-            }
-        }
-        bool gave_up = false;
-        for (int iter = 0; !__all(fresh); ++iter) {
-            bool ok = true;
-#pragma unroll
-            for (int k = 0; k < kRecPerLane; ++k) {
-                const int j = lane * K + k;
-                mr[k] = -INFINITY;
-                lr[k] = 0.0f;
-                if (k < K && j < Tb) {
-                    const unsigned long long r =
-                        __hip_atomic_load(rec + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok &= (r >> 32) != 0;
-                    mr[k] = __uint_as_float((uint32_t)r);
-                    lr[k] = __uint_as_float((uint32_t)(r >> 32));
-                }
-            }
-            if (__all(ok)) break;
-            if (iter >= spin_limit) {
-                gave_up = true;
+        const int t = it.t;
+        float M;
+        uint64_t W_t, W_t1, Z;
+        int last;
+        if constexpr (FROM_PREFIX) {
+            // the score pass's last split left the group's prefix: one word each
+            const unsigned long long* gp = p.gprefix + ((int64_t)it.b * p.Hq + hq) * (p.T + 2);
+            Z = gp[Tb];
+            W_t = gp[t];
+            W_t1 = gp[t + 1];
+            const unsigned long long ml = gp[p.T + 1];
+            M = __uint_as_float((uint32_t)ml);
+            last = (int)(ml >> 32);
+            if (Z == 0) {           // no score pass wrote it (Z >= 1 once one did)
                 if (lane == 0) {
                     __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     *fail = 1;
                 }
-                break;
+                continue;
             }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        if (gave_up) continue;      // the same in every lane of the wave
-        float mx = -INFINITY;
+        } else {
+            float mr[kRecPerLane], lr[kRecPerLane];
+            if (!read_records(p, record_of(p, it.b, hq, 0), Tb, K, spin_limit, mr, lr, fail)) continue;
+            GroupPrefix gpx = group_prefix(mr, lr, Tb, K);
+            M = gpx.M;
+            Z = gpx.Z;
+            last = gpx.last;
+            // W_t and W_{t+1} (exclusive prefixes of splits t and t+1)
+            const int kt = t & (K - 1);
+            const int kt1 = (t + 1) & (K - 1);
+            uint64_t at_t = 0, at_t1 = 0;
 #pragma unroll
-        for (int k = 0; k < kRecPerLane; ++k) mx = fmaxf(mx, mr[k]);
-        const float M = wave_max_f32(mx);
-        // lane-local exclusive prefix at the positions of splits t and t + 1
-        const int t = it.t;
-        const int kt = t & (K - 1);
-        const int kt1 = (t + 1) & (K - 1);
-        uint64_t run = 0, at_t = 0, at_t1 = 0;
-        int last = -1;
-#pragma unroll
-        for (int k = 0; k < kRecPerLane; ++k) {
-            const int j = lane * K + k;
-            uint64_t w = 0;
-            if (k < K && j < Tb) {
-                const double f = (double)mass_exp(mr[k] - M);
-                w = fixed40((double)lr[k] * f);
-                if (w) last = j;
+            for (int k = 0; k < kRecPerLane; ++k) {
+                if (k == kt) at_t = gpx.before[k];
+                if (k == kt1) at_t1 = gpx.before[k];
             }
-            if (k == kt) at_t = run;
-            if (k == kt1) at_t1 = run;
-            run += w;
+            W_t = lane_u64(gpx.excl + at_t, t >> ks);
+            W_t1 = (t + 1 < Tb) ? lane_u64(gpx.excl + at_t1, (t + 1) >> ks) : Z;
         }
-        const uint64_t incl = wave_scan_add_u64(run);
-        const uint64_t excl = incl - run;
-        const uint64_t Z = lane_u64(incl, 63);
-        last = wave_max_i32(last);
-        // W_t and W_{t+1} (exclusive prefixes of splits t and t+1)
-        const uint64_t mine_t = excl + at_t;
-        const uint64_t mine_t1 = excl + at_t1;
-        const uint64_t W_t = lane_u64(mine_t, t >> ks);
-        const uint64_t W_t1 = (t + 1 < Tb) ? lane_u64(mine_t1, (t + 1) >> ks) : Z;
 
         const double u0 = hs[h].u0;
         const double z = (double)Z * 0x1p-40;
@@ -1099,6 +1151,52 @@ __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& i
 #pragma unroll
                 for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, vals[e]);
             });
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Two-kernel path: the last split of a (sequence, KV head) to finish the score
+// pass computes the group's split-mass prefixes once, with the fused kernel's
+// arithmetic (read_records, group_prefix), so that each split of the sample
+// pass reads W_t, W_{t+1}, Z, M and the last split of positive mass instead of
+// every record of the sequence.  The count is the group's barrier word 0,
+// which the two-kernel path does not otherwise use; the last split returns it
+// to zero, and the sample pass's last split clears the prefixes.
+// ---------------------------------------------------------------------------
+template <int G, int NT>
+__device__ __forceinline__ void publish_group_prefix(const Params& p, const Item& it) {
+    constexpr int NW = NT / 64;
+    __shared__ int s_last;
+    __syncthreads();        // the workgroup's records are stored
+    if (threadIdx.x == 0) {
+        unsigned int* bar = p.barrier + ((int64_t)it.b * p.Hkv + it.g) * kBarrierStride;
+        const unsigned int prev = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = prev == (unsigned int)it.Tb - 1u;
+        if (s_last) __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int Tb = it.Tb;
+    const int K = 1 << (Tb <= 64 ? 0 : Tb <= 128 ? 1 : Tb <= 256 ? 2 : 3);
+    int fail = 0;
+    for (int h = wave; h < G; h += NW) {
+        const int hq = it.g * G + h;
+        float mr[kRecPerLane], lr[kRecPerLane];
+        // a give-up leaves the prefix at zero, which the sample pass reports
+        if (!read_records(p, record_of(p, it.b, hq, 0), Tb, K, kSpinLimit, mr, lr, &fail)) continue;
+        const GroupPrefix gpx = group_prefix(mr, lr, Tb, K);
+        unsigned long long* gp = p.gprefix + ((int64_t)it.b * p.Hq + hq) * (p.T + 2);
+#pragma unroll
+        for (int k = 0; k < kRecPerLane; ++k) {
+            const int j = lane * K + k;
+            if (k < K && j < Tb) gp[j] = gpx.excl + gpx.before[k];
+        }
+        if (lane == 0) {
+            gp[Tb] = gpx.Z;
+            gp[p.T + 1] = (unsigned long long)__float_as_uint(gpx.M) | ((unsigned long long)(uint32_t)gpx.last << 32);
         }
     }
 }
@@ -1141,7 +1239,8 @@ __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // workgroup.
 // ---------------------------------------------------------------------------
 template <int G, int D, int NT>
-__device__ __forceinline__ void finish_output(const Params& p, const Item& it, const int* fail) {
+__device__ __forceinline__ void finish_output(const Params& p, const Item& it, const int* fail,
+                                              bool clear_prefix = false) {
     __shared__ int s_last;
     wait_memory();           // this wave's slot additions have been performed
     __syncthreads();
@@ -1190,6 +1289,10 @@ __device__ __forceinline__ void finish_output(const Params& p, const Item& it, c
     if (p.mode == 0) {
         double* tg = p.targets + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * p.S;
         for (int i = threadIdx.x; i < G * p.S; i += NT) tg[i] = 0.0;
+    }
+    if (clear_prefix) {         // the two-kernel path's group prefixes
+        unsigned long long* gp = p.gprefix + ((int64_t)it.b * p.Hq + (int64_t)it.g * G) * (p.T + 2);
+        for (int i = threadIdx.x; i < G * (p.T + 2); i += NT) gp[i] = 0ull;
     }
 }
 

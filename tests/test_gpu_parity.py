@@ -172,11 +172,26 @@ def test_score_pass_intermediates():
         m = rec[..., 0].contiguous().view(torch.float32).double().numpy()
         l = rec[..., 1].contiguous().view(torch.float32).double().numpy()
         assert torch.all(torch.isnan(o.cpu()))      # o is written by the sample pass alone
+        # the group prefixes the score pass's last split leaves for the sample pass:
+        # [B, Hq, T + 2] words after the records, W_t (2^-40 fixed point), Z, M | last << 32
+        gp0 = lay.records_offset + B * Hq * T * 8
+        gp = wsc[gp0: gp0 + B * Hq * (T + 2) * 8].view(torch.int64).view(B, Hq, T + 2).numpy()
         w = x["workload"]
         for b in range(B):
             n = int(x["seq_lens"][b])
             Tb = -(-n // split)
             assert np.all(l[b, :, :Tb] >= 1.0) and np.all(rec[b, :, Tb:].numpy() == 0)
+            for h in range(Hq):
+                M = m[b, h, :Tb].max()
+                ml = int(gp[b, h, T + 1]) & 0xFFFFFFFFFFFFFFFF
+                assert np.float32(M) == np.array([ml & 0xFFFFFFFF], dtype=np.uint32).view(np.float32)[0]
+                masses = l[b, h, :Tb] * np.exp(m[b, h, :Tb] - M)
+                W = gp[b, h, :Tb + 1].astype(np.float64) * 2.0 ** -40
+                assert W[0] == 0 and np.all(np.diff(W) >= 0)
+                # fp32 exp of m_t - M: relative error up to about |m_t - M| * 2^-23
+                rt = 2.0 ** -22 * (1.0 + np.abs(m[b, h, :Tb] - M))
+                assert np.all(np.abs(np.diff(W) - masses) <= rt * masses + 2.0 ** -40)
+                assert (ml >> 32) == int(np.nonzero(np.diff(W) > 0)[0].max())
             for h in range(Hq):
                 kk, _ = H.head_rows(x, b, h // w.group)
                 q = x["q"][b, h].double().cpu().numpy()
