@@ -952,8 +952,11 @@ __device__ __forceinline__ void sample_head(const Params& p, const Item& it, con
                     x[u] = load16(vbase + off * E::bytes);
                 }
             }
+            // loads past the list were not issued: their terms are skipped too
+            // (the test is the same in every lane)
 #pragma unroll
-            for (int u = 0; u < UL; ++u) E::axpy16(wgt[u], x[u], acc);
+            for (int u = 0; u < UL; ++u)
+                if (r0 + u * RPL < nlist) E::axpy16(wgt[u], x[u], acc);
         }
         wave_lds_sync();       // the next chunk reuses the target area
     }
