@@ -318,4 +318,11 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 }
 __device__ __forceinline__ uint4 load16_stream(const void* p) { return load_stream(reinterpret_cast<const uint4*>(p)); }
 
+// The same hint for 16-byte stores of data written once (the stash, which the
+// sample pass reads once, and the zeros that return it to zero).
+typedef float stream_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(float4* p, const float4& v) {
+    __builtin_nontemporal_store((stream_f32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<stream_f32x4*>(p));
+}
+
 }  // namespace santa

@@ -59,7 +59,7 @@ void sample_kernel(Params p) {
             if (src[k]) {
                 const int i = threadIdx.x + k * NT;
                 reinterpret_cast<uint4*>(sc)[i] = v[k];
-                *src[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                store_stream(src[k], make_float4(0.0f, 0.0f, 0.0f, 0.0f));
             }
         }
     }

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
             split_stats<G, NT, true>(p, it, sc, reinterpret_cast<uint64_t*>(smem + L.prefix), hs);
             __syncthreads();
         }
-        write_stash<G, NT>(p, it, sc);
+        write_stash<G, NT, STATS>(p, it, sc);
         if constexpr (STATS) publish_group_prefix<G, NT>(p, it);
     }
 }

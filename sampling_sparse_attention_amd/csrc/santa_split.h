@@ -1314,7 +1314,10 @@ __device__ __forceinline__ void write_empty(const Params& p, const Item& it) {
 // (sc[h * split + local]) to stash row (b, g * G + h) at the split's first key,
 // with coalesced 16-byte stores.
 // ---------------------------------------------------------------------------
-template <int G, int NT>
+// STREAM: with the nontemporal hint (for the sample pass, which reads the
+// stash once, well after; the top-k selection reads it at once and is better
+// served from the caches).
+template <int G, int NT, bool STREAM = true>
 __device__ __forceinline__ void write_stash(const Params& p, const Item& it, const float* sc) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
@@ -1323,7 +1326,10 @@ __device__ __forceinline__ void write_stash(const Params& p, const Item& it, con
         float* dst = p.stash + ((int64_t)it.b * p.Hq + it.g * G + h) * p.stash_row + it.key0;
         for (int i = lane * 4; i < it.ns; i += 256) {
             if (i + 4 <= it.ns) {
-                *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(row + i);
+                if constexpr (STREAM)
+                    store_stream(reinterpret_cast<float4*>(dst + i), *reinterpret_cast<const float4*>(row + i));
+                else
+                    *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(row + i);
             } else {
                 for (int e = i; e < it.ns; ++e) dst[e] = row[e];
             }
