@@ -552,10 +552,20 @@ santa_status santa_decode_flash(const santa_shape* shape, const void* q, const v
         return fail(SANTA_STATUS_UNSUPPORTED,
                     "santa_decode_flash needs a sample for every tile: num_samples %d < %d splits",
                     num_samples, plan.T);
-    // (sequence, KV head)-fastest: the workgroups running together read the K
-    // rows of all KV heads of one range of tokens, which lie together in the
-    // token-major cache (split-fastest measured 10-40 % slower)
-    p.item_order = santa::kOrderHeadFastest;
+    // The workgroups running together read the K rows of all KV heads of one
+    // range of tokens, which lie together in the token-major cache
+    // (split-fastest measured 10-40 % slower).  A grid larger than the device,
+    // with T a multiple of 8, also keeps all KV heads of a split on one XCD
+    // (ragged 16-sequence batch: 154 -> 144 us); a resident grid keeps the
+    // head-fastest order, whose finishing times varied less from run to run
+    // (Llama-shaped step: 29.7 us against 29.7 or 31 us).
+    int dev = 0, cus = 0;
+    const int per_cu = santa::flash_blocks_per_cu(p, shape->dtype);
+    if (per_cu <= 0 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return fail(SANTA_STATUS_HIP_ERROR, "querying the device for the launch plan failed");
+    const bool resident = (int64_t)per_cu * cus >= (int64_t)p.items;
+    p.item_order = !resident && p.T % 8 == 0 ? santa::kOrderTokenBlocks : santa::kOrderHeadFastest;
     st = hip_check(santa::launch_flash(p, shape->dtype, static_cast<hipStream_t>(stream)),
                    "launching the flash decode kernel");
     if (st != SANTA_STATUS_OK) return st;

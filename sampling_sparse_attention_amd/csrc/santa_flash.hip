@@ -136,6 +136,35 @@ void flash_kernel(Params p) {
 }
 
 template <int G, int D, typename E>
+static const void* flash_fn() {
+    return reinterpret_cast<const void*>(&flash_kernel<G, D, E, kThreads>);
+}
+
+template <int D, typename E>
+static const void* flash_fn_g(int G) {
+    switch (G) {
+        case 1: return flash_fn<1, D, E>();
+        case 2: return flash_fn<2, D, E>();
+        case 4: return flash_fn<4, D, E>();
+        case 7: return flash_fn<7, D, E>();
+        case 8: return flash_fn<8, D, E>();
+        default: return nullptr;
+    }
+}
+
+// Workgroups of the flash kernel one compute unit holds at once (0: unknown).
+int flash_blocks_per_cu(const Params& p, int dtype) {
+    const void* fn = dtype == 0 ? (p.D == 64 ? flash_fn_g<64, Bf16>(p.G) : flash_fn_g<128, Bf16>(p.G))
+                                : (p.D == 64 ? flash_fn_g<64, F32>(p.G) : flash_fn_g<128, F32>(p.G));
+    if (!fn) return 0;
+    const size_t lds = split_lds_bytes(p.G, p.D, p.split, kThreads);
+    if (allow_lds(fn, lds) != hipSuccess) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, lds) != hipSuccess) return 0;
+    return n;
+}
+
+template <int G, int D, typename E>
 static hipError_t launch_flash_t(const Params& p, hipStream_t stream) {
     const size_t lds = split_lds_bytes(G, D, p.split, kThreads);
     const hipError_t e = allow_lds(reinterpret_cast<const void*>(&flash_kernel<G, D, E, kThreads>), lds);

@@ -123,6 +123,7 @@ hipError_t launch_clear(void* ws, size_t bytes, hipStream_t stream);
 hipError_t launch_flash(const Params& p, int dtype, hipStream_t stream);
 // Workgroups of the fused kernel one compute unit can hold at once (0 on error).
 int fused_blocks_per_cu(const Params& p, int dtype);
+int flash_blocks_per_cu(const Params& p, int dtype);
 // Bytes of LDS one workgroup may use on gfx950.
 constexpr size_t kLdsPerWorkgroup = 163840;
 

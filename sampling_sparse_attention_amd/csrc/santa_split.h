@@ -37,17 +37,18 @@ struct Item {
 };
 
 // Work item numbering (Params::item_order).
-//   kOrderTokenBlocks (fused kernel, T a multiple of 8): workgroups are handed
-//     to the 8 XCDs round-robin by index, so item i runs on XCD i mod 8; XCD x
-//     takes the splits t = x, x + 8, ... and, for each, the B * Hkv groups one
-//     after another: item = 8 * ((t / 8) * B * Hkv + b * Hkv + g) + t mod 8.
+//   kOrderTokenBlocks (fused kernel, and flash grids larger than the device;
+//     T a multiple of 8): workgroups are handed to the 8 XCDs round-robin by
+//     index, so item i runs on XCD i mod 8; XCD x takes the splits t = x,
+//     x + 8, ... and, for each, the B * Hkv groups one after another:
+//     item = 8 * ((t / 8) * B * Hkv + b * Hkv + g) + t mod 8.
 //     The KV heads of a token-major cache share every token row, so the
 //     workgroups reading one stretch of rows run together on one XCD and the
 //     rows are fetched together (1.4 us less K stream on the Llama-shaped
 //     step than with the order below); every group still streams across the
 //     whole launch, so the groups reach their barriers together at the end of
 //     the K stream and their latency-bound tails run side by side.
-//   kOrderHeadFastest (fused kernel otherwise, S^2ANTA-flash): item = t * B *
+//   kOrderHeadFastest (fused and flash kernels otherwise): item = t * B *
 //     Hkv + b * Hkv + g, with the same side-by-side tails.
 //   kOrderSplitFastest (two-kernel path, whose grids are larger than the
 //     device): item = (b * Hkv + g) * T + t, so that a group's splits run close
