@@ -150,7 +150,7 @@ typedef struct santa_shape {
  *            the last of them;
  *   flash    santa_decode_flash only: per (sequence, query head) a 64-bit
  *            reference maximum, then (256-byte aligned) fp64 accumulators
- *            [B, Hkv, 8, G, d + 2] of weighted tile means and weights;
+ *            [B, Hkv, 4, G, d + 2] of weighted tile means and weights;
  *   records  [B, Hq, num_splits] x 8 bytes: per split the maximum score m and
  *            l = sum exp(s_i - m) (the tile partition functions of section 3.2,
  *            Pass 1) as one word, fp32 l in the high and fp32 m in the low half

@@ -131,9 +131,9 @@ santa_status make_plan(const santa_shape* s, int32_t S, int32_t mode, Plan* plan
     L.flash_offset = align256(L.accum_offset + (size_t)s->batch * s->num_q_heads * santa::kOutSlots *
                                                    s->head_dim * sizeof(float));
     // flash region: reference maxima [B, Hq] u64, then (256-aligned) the fp64
-    // accumulators [B, Hkv, kOutSlots, G, d + 2]
+    // accumulators [B, Hkv, kFlashSlots, G, d + 2]
     L.records_offset = align256(L.flash_offset + align256(rows * sizeof(unsigned long long)) +
-                                (size_t)s->batch * s->num_q_heads * santa::kOutSlots * (s->head_dim + 2) *
+                                (size_t)s->batch * s->num_q_heads * santa::kFlashSlots * (s->head_dim + 2) *
                                     sizeof(double));
     // split records [B, Hq, T], then the group prefixes [B, Hq, T + 2]
     L.stash_offset = align256(L.records_offset + rows * (size_t)T * 8 + rows * (size_t)(T + 2) * 8);

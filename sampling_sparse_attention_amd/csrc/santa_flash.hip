@@ -58,7 +58,7 @@ void flash_kernel(Params p) {
     const int off = it.t * per + min(it.t, rem);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    double* acc_group = p.flash_acc + ((int64_t)it.b * p.Hkv + it.g) * kOutSlots * G * DA;
+    double* acc_group = p.flash_acc + ((int64_t)it.b * p.Hkv + it.g) * kFlashSlots * G * DA;
     for (int h = wave; h < G; h += NW) {
         const int hq = it.g * G + h;
         float r = 0.0f;
@@ -84,7 +84,7 @@ void flash_kernel(Params p) {
         }
         wave_lds_sync();
         const HeadState st = hs[h];
-        double* slot = acc_group + ((it.t % kOutSlots) * G + h) * DA;
+        double* slot = acc_group + ((it.t % kFlashSlots) * G + h) * DA;
         double w = 0.0;
         // two keys at a time and four V loads per lane in flight: this kernel holds
         // more state across the sampling, and a tile samples few rows
@@ -120,14 +120,14 @@ void flash_kernel(Params p) {
         const int h = i / D, e = i - h * D;
         double num = 0.0, den = 0.0;
 #pragma unroll
-        for (int k = 0; k < kOutSlots; ++k) {
+        for (int k = 0; k < kFlashSlots; ++k) {
             num += load_acc((k * G + h) * DA + e);
             den += load_acc((k * G + h) * DA + D);
         }
         o[i] = (float)(num / den);
     }
     __syncthreads();            // every thread has read the slots before they are cleared
-    for (int i = threadIdx.x; i < kOutSlots * G * DA; i += NT)
+    for (int i = threadIdx.x; i < kFlashSlots * G * DA; i += NT)
         __hip_atomic_store(acc_bits + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x < G)
         __hip_atomic_store(p.flash_ref + (int64_t)it.b * p.Hq + it.g * G + threadIdx.x, 0ull, __ATOMIC_RELAXED,

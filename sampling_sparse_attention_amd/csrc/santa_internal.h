@@ -46,6 +46,10 @@ constexpr int kBarrierStride = 32 * kBarrierLines;   // 32-bit words per (sequen
 // (split % kOutSlots) of its (sequence, KV head), so few additions meet on one
 // word; the last split to finish sums the slots into o and clears them.
 constexpr int kOutSlots = 8;
+// S^2ANTA-flash's fp64 slots: fewer than the fused kernel's, since its last
+// split reads and clears twice the bytes per slot (Llama-shaped step: 29.6 us
+// with 8, 28.2 us with 4, 32.7 us with 2)
+constexpr int kFlashSlots = 4;
 
 // Orders of the work items (sequence, KV head, split) over the workgroup indices.
 constexpr int kOrderSplitFastest = 0;
@@ -65,7 +69,7 @@ struct Params {
     unsigned long long* gprefix;  // two-kernel path: [B * Hq][T + 2] split-mass prefixes W_t, Z, then M | last << 32
     unsigned int* barrier;        // [B * Hkv] x kBarrierStride words: counts, flags
     float* accum;                 // [B * Hkv][kOutSlots][G * D] partial outputs (zero between calls)
-    double* flash_acc;            // S^2ANTA-flash: [B * Hkv][kOutSlots][G][D + 2] weighted sums, weight
+    double* flash_acc;            // S^2ANTA-flash: [B * Hkv][kFlashSlots][G][D + 2] weighted sums, weight
     unsigned long long* flash_ref;   // S^2ANTA-flash: [B, Hq] reference maximum (1 << 32 | bits), 0 unset
     float* stash;                 // [B, Hq, T * split] scaled scores (two-kernel path)
     double* targets;              // [B, Hq, S] sorted uniforms (multinomial only)

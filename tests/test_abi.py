@@ -195,7 +195,7 @@ def test_flash_rejects_multinomial_and_too_few_samples_before_launch(lib):
     assert call(0, 2) == INVALID
     lay = santa.santa_workspace_layout_query(shape, 64, 2)
     assert lay.accum_offset < lay.flash_offset < lay.records_offset
-    assert lay.records_offset - lay.flash_offset >= 256 + 32 * 8 * 130 * 8   # refs, then 8 fp64 slots per head
+    assert lay.records_offset - lay.flash_offset >= 256 + 32 * 4 * 130 * 8   # refs, then 4 fp64 slots per head
 
 
 def test_args_struct_matches_header_layout(lib):
