@@ -31,6 +31,8 @@ void sample_kernel(Params p) {
         s_fail = 0;
         s_err = err0;
     }
+    // the group's prefix words, in flight with the stash loads
+    const uint64_t words = load_group_prefix_words<G, NT>(p, it);
     load_pages<NT>(p, it, pages);
     // the split's stash slice in 16-byte pieces, all loads issued before any
     // store; a piece that starts below ns may reach past it, but stays inside
@@ -74,7 +76,7 @@ void sample_kernel(Params p) {
     // the group's prefix comes from the score pass's last split (an earlier
     // launch): one missing now means no score pass preceded this one, which is
     // an error, not a wait
-    prefix_and_sample<G, D, E, NT, true>(p, it, L, smem, 0, &s_fail);
+    prefix_and_sample<G, D, E, NT, true>(p, it, L, smem, 0, &s_fail, words);
     finish_output<G, D, NT>(p, it, &s_fail, true);
 }
 

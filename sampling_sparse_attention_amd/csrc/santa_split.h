@@ -1076,9 +1076,30 @@ __device__ __forceinline__ GroupPrefix group_prefix(const float (&mr)[kRecPerLan
 // and the head is skipped: nothing is computed from an incomplete set of
 // records.
 // ---------------------------------------------------------------------------
+// The two-kernel path's group-prefix words of the heads a wave samples,
+// loaded before the sample pass needs them (the score pass, an earlier launch,
+// wrote them): lane 4 s + k of the wave holds, for its s-th head h = wave +
+// s * NW, word k of Z = P[Tb], W_t = P[t], W_t+1 = P[t + 1] and M | last << 32
+// = P[T + 1], where P is the head's [T + 2] prefix row.
+template <int G, int NT>
+__device__ __forceinline__ uint64_t load_group_prefix_words(const Params& p, const Item& it) {
+    constexpr int NW = NT / 64;
+    constexpr int HPW = (G + NW - 1) / NW;     // heads per wave, at most
+    static_assert(4 * HPW <= 64, "one lane per word");
+    const int lane = threadIdx.x & 63;
+    const int h = (threadIdx.x >> 6) + (lane >> 2) * NW;
+    if (lane >= 4 * HPW || h >= G) return 0ull;
+    const unsigned long long* gp = p.gprefix + ((int64_t)it.b * p.Hq + it.g * G + h) * (p.T + 2);
+    const int k = lane & 3;
+    return gp[k == 0 ? it.Tb : k == 1 ? it.t : k == 2 ? it.t + 1 : p.T + 1];
+}
+
+// FROM_PREFIX: the group's prefix words come from load_group_prefix_words
+// (`words`), otherwise from the split records.
 template <int G, int D, typename E, int NT, bool FROM_PREFIX = false, int KW = 4, int UL = 8>
 __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
-                                                  unsigned char* smem, int spin_limit, int* fail) {
+                                                  unsigned char* smem, int spin_limit, int* fail,
+                                                  uint64_t words = 0) {
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
@@ -1095,11 +1116,11 @@ __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& i
         int last;
         if constexpr (FROM_PREFIX) {
             // the score pass's last split left the group's prefix: one word each
-            const unsigned long long* gp = p.gprefix + ((int64_t)it.b * p.Hq + hq) * (p.T + 2);
-            Z = gp[Tb];
-            W_t = gp[t];
-            W_t1 = gp[t + 1];
-            const unsigned long long ml = gp[p.T + 1];
+            const int s4 = 4 * ((h - wave) / NW);
+            Z = lane_u64(words, s4);
+            W_t = lane_u64(words, s4 + 1);
+            W_t1 = lane_u64(words, s4 + 2);
+            const uint64_t ml = lane_u64(words, s4 + 3);
             M = __uint_as_float((uint32_t)ml);
             last = (int)(ml >> 32);
             if (Z == 0) {           // no score pass wrote it (Z >= 1 once one did)
