@@ -1094,14 +1094,200 @@ __device__ __forceinline__ uint64_t load_group_prefix_words(const Params& p, con
     return gp[k == 0 ? it.Tb : k == 1 ? it.t : k == 2 ? it.t + 1 : p.T + 1];
 }
 
+// Sampling and gather-and-add for two heads of one wave whose target ranges
+// hold at most kFewTargets targets each (the sample pass, G > NW): both heads'
+// distinct keys are found first (head B's kept one per lane while head A's
+// fill the wave's target area), then one gather loop reads the rows of both
+// lists with all their loads in flight together, so the wave waits for one
+// round of V loads instead of one per head.  Per head the rows are added with
+// the same count weights as sample_head; only the order of the fp32 sums of
+// the second head's rows differs.
+template <int G, int D, typename E, int UL = 4>
+__device__ __forceinline__ void sample_pair(const Params& p, const Item& it, const HeadState& sA, int hA, int nA,
+                                            const HeadState& sB, int hB, int nB, const LdsLayout& L,
+                                            unsigned char* smem, float* slotA, float* slotB) {
+    constexpr int LPR = D * E::bytes / 16;
+    constexpr int RPL = 64 / LPR;
+    constexpr int ELV = 16 / E::bytes;
+    constexpr int EL = D / 64;
+    static_assert(kFewTargets <= 64 && RPL * LPR == 64 && ELV == EL * RPL, "row shape");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rsub = lane / LPR;
+    const int piece = lane % LPR;
+    TargetArea* ta = reinterpret_cast<TargetArea*>(smem + L.scratch) + wave;
+    const int* pages = reinterpret_cast<const int*>(smem + L.pages);
+    const char* vbase = reinterpret_cast<const char*>(p.v);
+    auto sample_list = [&](const HeadState& st, int h, int na) -> int {
+        const int hq = it.g * G + h;
+        const uint64_t* ph = reinterpret_cast<const uint64_t*>(smem + L.prefix) + h * p.split;
+        if (p.mode == 2) return sample_few<2>(p, it, st, hq, ph, ta, st.m_lo, na, lane);
+        if (p.mode == 1) return sample_few<1>(p, it, st, hq, ph, ta, st.m_lo, na, lane);
+        return sample_chunk_multinomial(p, it, st, hq, ph, ta, st.m_lo, na, lane);
+    };
+    // head B's distinct keys, entry j in lane j (lanes past the list hold key 0
+    // with count 0: key 0 is a row of every split)
+    int nlB = 0, keyB = 0;
+    unsigned int cntB = 0;
+    if (nB > 0) {
+        nlB = sample_list(sB, hB, nB);
+        if (lane < nlB) {
+            keyB = ta->lkey[lane];
+            cntB = ta->lcnt[lane];
+        }
+        wave_lds_sync();        // head A's sampling reuses the target area
+    }
+    const int nlA = nA > 0 ? sample_list(sA, hA, nA) : 0;
+    const int ntot = nlA + nlB;
+    float accA[ELV], accB[ELV];
+#pragma unroll
+    for (int e = 0; e < ELV; ++e) accA[e] = accB[e] = 0.0f;
+    for (int r0 = 0; r0 < ntot; r0 += UL * RPL) {
+        uint4 x[UL];
+        float wa[UL], wb[UL];
+#pragma unroll
+        for (int u = 0; u < UL; ++u) {
+            const int row = r0 + u * RPL + rsub;
+            // head B's entry of this row from the lane holding it (every lane
+            // takes part in the exchange)
+            const int jb = min(max(row - nlA, 0), 63);
+            const int kb = __shfl(keyB, jb, 64);
+            const unsigned int cb = (unsigned int)__shfl((int)cntB, jb, 64);
+            wa[u] = 0.0f;
+            wb[u] = 0.0f;
+            x[u] = make_uint4(0u, 0u, 0u, 0u);
+            // a load whose rows all lie past both lists is not issued (the test
+            // is the same in every lane); a row past them within an issued load
+            // reads key 0 with weight 0
+            if (r0 + u * RPL < ntot) {
+                int key = kb;
+                if (row < nlA) {
+                    key = ta->lkey[row];
+                    wa[u] = (float)ta->lcnt[row];
+                } else if (row < ntot) {
+                    wb[u] = (float)cb;
+                }
+                const int64_t off = row_offset(p, it, key, pages) + piece * ELV;
+                x[u] = load16(vbase + off * E::bytes);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UL; ++u)
+            if (r0 + u * RPL < ntot) {
+                E::axpy16(wa[u], x[u], accA);
+                E::axpy16(wb[u], x[u], accB);
+            }
+    }
+    wave_lds_sync();            // the target area is free again
+#pragma unroll
+    for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+        for (int e = 0; e < ELV; ++e) {
+            accA[e] += __shfl_xor(accA[e], m, 64);
+            accB[e] += __shfl_xor(accB[e], m, 64);
+        }
+    const int col = piece * ELV + rsub * EL;
+    if (nA > 0)
+#pragma unroll
+        for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slotA + col + e, accA[rsub * EL + e]);
+    if (nB > 0)
+#pragma unroll
+        for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slotB + col + e, accB[rsub * EL + e]);
+}
+
+// prefix_and_sample of the sample pass for G > NW (two heads on some waves):
+// the same per-head steps, from the group's prefix words (`words`), but a wave
+// whose two heads each hold at most kFewTargets targets samples both before
+// gathering their rows together (sample_pair).
+template <int G, int D, typename E, int NT, int KW, int UL>
+__device__ __forceinline__ void prefix_and_sample_pairs(const Params& p, const Item& it, const LdsLayout& L,
+                                                        unsigned char* smem, int* fail, uint64_t words) {
+    HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
+    constexpr int NW = NT / 64;
+    static_assert(G > NW && G <= 2 * NW, "one or two heads per wave");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // head h's group prefix, target range and state; false if the head is to
+    // be skipped (its prefix is missing: the error is set)
+    auto setup = [&](int h, HeadState& st) -> bool {
+        const int hq = it.g * G + h;
+        const int t = it.t;
+        // the score pass's last split left the group's prefix: one word each
+        const int s4 = 4 * ((h - wave) / NW);
+        const uint64_t Z = lane_u64(words, s4);
+        const uint64_t W_t = lane_u64(words, s4 + 1);
+        const uint64_t W_t1 = lane_u64(words, s4 + 2);
+        const uint64_t ml = lane_u64(words, s4 + 3);
+        const float M = __uint_as_float((uint32_t)ml);
+        const int last = (int)(ml >> 32);
+        if (Z == 0) {               // no score pass wrote it (Z >= 1 once one did)
+            if (lane == 0) {
+                __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *fail = 1;
+            }
+            return false;
+        }
+        const double u0 = hs[h].u0;
+        const double z = (double)Z * 0x1p-40;
+        const double w_lo = (double)W_t * 0x1p-40;
+        const double w_hi = (double)W_t1 * 0x1p-40;
+        int m_lo, m_hi;
+        if (p.mode == 2) target_range<2>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
+        else if (p.mode == 1) target_range<1>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
+        else target_range<0>(p, it.b, hq, z, u0, w_lo, w_hi, t == last, lane, &m_lo, &m_hi);
+        // the head's state in registers (every value here is the same in all lanes)
+        st = hs[h];
+        st.w_lo = w_lo;
+        st.z = z;
+        st.f = (double)mass_exp(st.m_t - M);
+        st.inv_f = (double)mass_exp(M - st.m_t);
+        st.m_lo = m_lo;
+        st.m_hi = max(m_hi, m_lo);
+        st.n_targets = p.S;
+        st.stream = 0;
+        st.off = 0;
+        return true;
+    };
+    // into accumulation slot t mod kOutSlots of the group
+    auto slot_of = [&](int h) {
+        return p.accum + ((((int64_t)it.b * p.Hkv + it.g) * kOutSlots + it.t % kOutSlots) * G + h) * D;
+    };
+    auto one_head = [&](const HeadState& st, int h) {
+        float* slot = slot_of(h);
+        sample_head<G, D, E, KW, UL>(p, it, st, h, L, smem, [&](int col, const float* vals) {
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, vals[e]);
+        });
+    };
+    const int hA = wave, hB = wave + NW;
+    HeadState sA;
+    const int nA = setup(hA, sA) ? sA.m_hi - sA.m_lo : 0;
+    if (hB >= G) {                  // one head on this wave
+        if (nA > 0) one_head(sA, hA);
+        return;
+    }
+    HeadState sB;
+    const int nB = setup(hB, sB) ? sB.m_hi - sB.m_lo : 0;
+    if (nA <= kFewTargets && nB <= kFewTargets) {
+        sample_pair<G, D, E>(p, it, sA, hA, nA, sB, hB, nB, L, smem, slot_of(hA), slot_of(hB));
+    } else {
+        if (nA > 0) one_head(sA, hA);
+        if (nB > 0) one_head(sB, hB);
+    }
+}
+
 // FROM_PREFIX: the group's prefix words come from load_group_prefix_words
 // (`words`), otherwise from the split records.
 template <int G, int D, typename E, int NT, bool FROM_PREFIX = false, int KW = 4, int UL = 8>
 __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
                                                   unsigned char* smem, int spin_limit, int* fail,
                                                   uint64_t words = 0) {
-    HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
     constexpr int NW = NT / 64;
+    if constexpr (FROM_PREFIX && G > NW) {
+        prefix_and_sample_pairs<G, D, E, NT, KW, UL>(p, it, L, smem, fail, words);
+        return;
+    }
+    HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int Tb = it.Tb;
