@@ -1095,7 +1095,7 @@ __device__ __forceinline__ uint64_t load_group_prefix_words(const Params& p, con
 }
 
 // Sampling and gather-and-add for two heads of one wave whose target ranges
-// hold at most kFewTargets targets each (the sample pass, G > NW): both heads'
+// hold at most kFewTargets targets each (groups of more heads than waves): both heads'
 // distinct keys are found first (head B's kept one per lane while head A's
 // fill the wave's target area), then one gather loop reads the rows of both
 // lists with all their loads in flight together, so the wave waits for one
@@ -1195,37 +1195,62 @@ __device__ __forceinline__ void sample_pair(const Params& p, const Item& it, con
         for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slotB + col + e, accB[rsub * EL + e]);
 }
 
-// prefix_and_sample of the sample pass for G > NW (two heads on some waves):
-// the same per-head steps, from the group's prefix words (`words`), but a wave
-// whose two heads each hold at most kFewTargets targets samples both before
-// gathering their rows together (sample_pair).
-template <int G, int D, typename E, int NT, int KW, int UL>
+// prefix_and_sample for G > NW (two heads on some waves): the same per-head
+// steps, but a wave whose two heads each hold at most kFewTargets targets
+// samples both before gathering their rows together (sample_pair).
+template <int G, int D, typename E, int NT, bool FROM_PREFIX, int KW, int UL>
 __device__ __forceinline__ void prefix_and_sample_pairs(const Params& p, const Item& it, const LdsLayout& L,
-                                                        unsigned char* smem, int* fail, uint64_t words) {
+                                                        unsigned char* smem, int spin_limit, int* fail,
+                                                        uint64_t words) {
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);
     constexpr int NW = NT / 64;
     static_assert(G > NW && G <= 2 * NW, "one or two heads per wave");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int Tb = it.Tb;
+    const int ks = Tb <= 64 ? 0 : Tb <= 128 ? 1 : Tb <= 256 ? 2 : 3;
+    const int K = 1 << ks;
     // head h's group prefix, target range and state; false if the head is to
-    // be skipped (its prefix is missing: the error is set)
+    // be skipped (its records or prefix are missing: the error is set)
     auto setup = [&](int h, HeadState& st) -> bool {
         const int hq = it.g * G + h;
         const int t = it.t;
-        // the score pass's last split left the group's prefix: one word each
-        const int s4 = 4 * ((h - wave) / NW);
-        const uint64_t Z = lane_u64(words, s4);
-        const uint64_t W_t = lane_u64(words, s4 + 1);
-        const uint64_t W_t1 = lane_u64(words, s4 + 2);
-        const uint64_t ml = lane_u64(words, s4 + 3);
-        const float M = __uint_as_float((uint32_t)ml);
-        const int last = (int)(ml >> 32);
-        if (Z == 0) {               // no score pass wrote it (Z >= 1 once one did)
-            if (lane == 0) {
-                __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                *fail = 1;
+        float M;
+        uint64_t W_t, W_t1, Z;
+        int last;
+        if constexpr (FROM_PREFIX) {
+            // the score pass's last split left the group's prefix: one word each
+            const int s4 = 4 * ((h - wave) / NW);
+            Z = lane_u64(words, s4);
+            W_t = lane_u64(words, s4 + 1);
+            W_t1 = lane_u64(words, s4 + 2);
+            const uint64_t ml = lane_u64(words, s4 + 3);
+            M = __uint_as_float((uint32_t)ml);
+            last = (int)(ml >> 32);
+            if (Z == 0) {           // no score pass wrote it (Z >= 1 once one did)
+                if (lane == 0) {
+                    __hip_atomic_store(&p.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    *fail = 1;
+                }
+                return false;
             }
-            return false;
+        } else {
+            float mr[kRecPerLane], lr[kRecPerLane];
+            if (!read_records(p, record_of(p, it.b, hq, 0), Tb, K, spin_limit, mr, lr, fail)) return false;
+            GroupPrefix gpx = group_prefix(mr, lr, Tb, K);
+            M = gpx.M;
+            Z = gpx.Z;
+            last = gpx.last;
+            const int kt = t & (K - 1);
+            const int kt1 = (t + 1) & (K - 1);
+            uint64_t at_t = 0, at_t1 = 0;
+#pragma unroll
+            for (int k = 0; k < kRecPerLane; ++k) {
+                if (k == kt) at_t = gpx.before[k];
+                if (k == kt1) at_t1 = gpx.before[k];
+            }
+            W_t = lane_u64(gpx.excl + at_t, t >> ks);
+            W_t1 = (t + 1 < Tb) ? lane_u64(gpx.excl + at_t1, (t + 1) >> ks) : Z;
         }
         const double u0 = hs[h].u0;
         const double z = (double)Z * 0x1p-40;
@@ -1277,14 +1302,15 @@ __device__ __forceinline__ void prefix_and_sample_pairs(const Params& p, const I
 }
 
 // FROM_PREFIX: the group's prefix words come from load_group_prefix_words
-// (`words`), otherwise from the split records.
+// (`words`), otherwise from the split records.  Groups of more heads than
+// waves take prefix_and_sample_pairs.
 template <int G, int D, typename E, int NT, bool FROM_PREFIX = false, int KW = 4, int UL = 8>
 __device__ __forceinline__ void prefix_and_sample(const Params& p, const Item& it, const LdsLayout& L,
                                                   unsigned char* smem, int spin_limit, int* fail,
                                                   uint64_t words = 0) {
     constexpr int NW = NT / 64;
-    if constexpr (FROM_PREFIX && G > NW) {
-        prefix_and_sample_pairs<G, D, E, NT, KW, UL>(p, it, L, smem, fail, words);
+    if constexpr (G > NW) {
+        prefix_and_sample_pairs<G, D, E, NT, FROM_PREFIX, KW, UL>(p, it, L, smem, spin_limit, fail, words);
         return;
     }
     HeadState* hs = reinterpret_cast<HeadState*>(smem + L.heads);

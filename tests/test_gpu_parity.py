@@ -138,15 +138,17 @@ def test_two_stage_calls_equal_decode():
 @pytest.mark.parametrize("G", [7, 8])
 @pytest.mark.parametrize("mode", [0, 1, 2])
 def test_two_stage_two_heads_per_wave(G, mode):
-    """Groups of 7 and 8 heads on four waves in the sample pass: a wave samples
-    two heads and, when each has at most 32 targets in its split, gathers both
-    heads' rows in one loop; a dominant sink gives splits where a head holds
-    more than that (the one-head-at-a-time gather) and splits where a head
-    holds none.  Against the oracle, and the same indices as the fused path."""
+    """Groups of 7 and 8 heads on four waves, in the sample pass and in the fused
+    kernel: a wave samples two heads and, when each has at most 32 targets in
+    its split, gathers both heads' rows in one loop; a dominant sink gives
+    splits where a head holds more than that (the one-head-at-a-time gather)
+    and splits where a head holds none.  Both paths against the oracle, with
+    the same indices."""
     x = _inputs(G=G, lens=(900, 1200), q_scale=4.0, sinks=1)
     o2, i2, _, _ = H.run_hip(x, 256, mode, seed=31, split=128, stages="split")
     print(H.check_all(x, 256, mode, 31, o2, i2))
     o1, i1, _, _ = H.run_hip(x, 256, mode, seed=31, split=128)
+    print(H.check_all(x, 256, mode, 31, o1, i1))
     assert torch.equal(i1, i2)
     assert torch.allclose(o1, o2, rtol=1e-5, atol=1e-6)
     # the case mix this test is for: per (sequence, head, split) target counts
