@@ -59,43 +59,78 @@ void flash_kernel(Params p) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     double* acc_group = p.flash_acc + ((int64_t)it.b * p.Hkv + it.g) * kFlashSlots * G * DA;
-    for (int h = wave; h < G; h += NW) {
+    // lane 0: publishes or reads head h's reference maximum r (returned) and
+    // puts the tile's sampling state of head h into hs[h]
+    auto tile_setup = [&](int h) -> float {
         const int hq = it.g * G + h;
-        float r = 0.0f;
-        if (lane == 0) {
-            unsigned long long* ref = p.flash_ref + (int64_t)it.b * p.Hq + hq;
-            unsigned long long seen = 0ull;
-            const unsigned long long mine = (1ull << 32) | __float_as_uint(hs[h].m_t);
-            __hip_atomic_compare_exchange_strong(ref, &seen, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-            r = seen == 0ull ? hs[h].m_t : __uint_as_float((uint32_t)seen);
-            // the tile's own CDF: edges P_j in units of its fixed-point masses
-            const double z = fixed_to_double(prefix[h * p.split + it.ns - 1]);
-            hs[h].w_lo = 0.0;
-            hs[h].f = 1.0;
-            hs[h].inv_f = 1.0;
-            hs[h].z = z;
-            hs[h].u0 = p.mode == 2 ? uniform01(p.seed, it.b, hq, 0ull, (uint64_t)(1 + it.t)) : 0.0;
-            hs[h].m_lo = off;
-            hs[h].m_hi = off + n_t;
-            hs[h].n_targets = n_t;
-            hs[h].stream = 1 + it.t;
-            hs[h].off = off;
+        unsigned long long* ref = p.flash_ref + (int64_t)it.b * p.Hq + hq;
+        unsigned long long seen = 0ull;
+        const unsigned long long mine = (1ull << 32) | __float_as_uint(hs[h].m_t);
+        __hip_atomic_compare_exchange_strong(ref, &seen, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        const float r = seen == 0ull ? hs[h].m_t : __uint_as_float((uint32_t)seen);
+        // the tile's own CDF: edges P_j in units of its fixed-point masses
+        const double z = fixed_to_double(prefix[h * p.split + it.ns - 1]);
+        hs[h].w_lo = 0.0;
+        hs[h].f = 1.0;
+        hs[h].inv_f = 1.0;
+        hs[h].z = z;
+        hs[h].u0 = p.mode == 2 ? uniform01(p.seed, it.b, hq, 0ull, (uint64_t)(1 + it.t)) : 0.0;
+        hs[h].m_lo = off;
+        hs[h].m_hi = off + n_t;
+        hs[h].n_targets = n_t;
+        hs[h].stream = 1 + it.t;
+        hs[h].off = off;
+        return r;
+    };
+    auto slot_of = [&](int h) { return acc_group + ((it.t % kFlashSlots) * G + h) * DA; };
+    // the tile's weight relative to the shared reference r, and 1/S_t, applied
+    // to a head's sum of rows; the compare-and-swap's result is first needed
+    // here, after the gather
+    auto add_tile = [&](double* slot, const HeadState& st, float r, double& w, int col, const float* vals) {
+        w = st.z * exp((double)st.m_t - (double)__shfl(r, 0, 64));
+        const double scale = w / (double)n_t;
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, scale * (double)vals[e]);
+    };
+    int h_first = wave;
+    if constexpr (G > NW) {
+        // two heads on this wave with few samples each: both tiles' states
+        // first, then one gather of both heads' rows
+        static_assert(G <= 2 * NW, "one or two heads per wave");
+        const int hA = wave, hB = wave + NW;
+        if (hB < G && n_t <= kFewTargets) {
+            float rA = 0.0f, rB = 0.0f;
+            if (lane == 0) {
+                rA = tile_setup(hA);
+                rB = tile_setup(hB);
+            }
+            wave_lds_sync();
+            const HeadState stA = hs[hA], stB = hs[hB];
+            double* slotA = slot_of(hA);
+            double* slotB = slot_of(hB);
+            double wA = 0.0, wB = 0.0;
+            sample_pair<G, D, E>(p, it, stA, hA, n_t, stB, hB, n_t, L, smem,
+                                 [&](int col, const float* vals) { add_tile(slotA, stA, rA, wA, col, vals); },
+                                 [&](int col, const float* vals) { add_tile(slotB, stB, rB, wB, col, vals); });
+            if (lane == 0) {
+                unsafeAtomicAdd(slotA + D, wA);
+                unsafeAtomicAdd(slotB + D, wB);
+            }
+            h_first = G;
         }
+    }
+    for (int h = h_first; h < G; h += NW) {
+        float r = 0.0f;
+        if (lane == 0) r = tile_setup(h);
         wave_lds_sync();
         const HeadState st = hs[h];
-        double* slot = acc_group + ((it.t % kFlashSlots) * G + h) * DA;
+        double* slot = slot_of(h);
         double w = 0.0;
         // two keys at a time and four V loads per lane in flight: this kernel holds
         // more state across the sampling, and a tile samples few rows
-        sample_head<G, D, E, 2, 4>(p, it, st, h, L, smem, [&](int col, const float* vals) {
-            // the tile's weight relative to the shared reference r, and 1/S_t; the
-            // compare-and-swap's result is first needed here, after the gather
-            w = st.z * exp((double)st.m_t - (double)__shfl(r, 0, 64));
-            const double scale = w / (double)n_t;
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slot + col + e, scale * (double)vals[e]);
-        });
+        sample_head<G, D, E, 2, 4>(p, it, st, h, L, smem,
+                                   [&](int col, const float* vals) { add_tile(slot, st, r, w, col, vals); });
         if (lane == 0) unsafeAtomicAdd(slot + D, w);
     }
 

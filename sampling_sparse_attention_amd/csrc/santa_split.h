@@ -1101,11 +1101,12 @@ __device__ __forceinline__ uint64_t load_group_prefix_words(const Params& p, con
 // lists with all their loads in flight together, so the wave waits for one
 // round of V loads instead of one per head.  Per head the rows are added with
 // the same count weights as sample_head; only the order of the fp32 sums of
-// the second head's rows differs.
-template <int G, int D, typename E, int UL = 4>
+// the second head's rows differs.  Each head with targets passes its sum to
+// its emit(col, vals) as sample_head does.
+template <int G, int D, typename E, int UL = 4, typename EmitA, typename EmitB>
 __device__ __forceinline__ void sample_pair(const Params& p, const Item& it, const HeadState& sA, int hA, int nA,
                                             const HeadState& sB, int hB, int nB, const LdsLayout& L,
-                                            unsigned char* smem, float* slotA, float* slotB) {
+                                            unsigned char* smem, EmitA&& emitA, EmitB&& emitB) {
     constexpr int LPR = D * E::bytes / 16;
     constexpr int RPL = 64 / LPR;
     constexpr int ELV = 16 / E::bytes;
@@ -1187,12 +1188,17 @@ __device__ __forceinline__ void sample_pair(const Params& p, const Item& it, con
             accB[e] += __shfl_xor(accB[e], m, 64);
         }
     const int col = piece * ELV + rsub * EL;
-    if (nA > 0)
+    float vals[EL];
+    if (nA > 0) {
 #pragma unroll
-        for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slotA + col + e, accA[rsub * EL + e]);
-    if (nB > 0)
+        for (int e = 0; e < EL; ++e) vals[e] = accA[rsub * EL + e];
+        emitA(col, vals);
+    }
+    if (nB > 0) {
 #pragma unroll
-        for (int e = 0; e < EL; ++e) unsafeAtomicAdd(slotB + col + e, accB[rsub * EL + e]);
+        for (int e = 0; e < EL; ++e) vals[e] = accB[rsub * EL + e];
+        emitB(col, vals);
+    }
 }
 
 // prefix_and_sample for G > NW (two heads on some waves): the same per-head
@@ -1294,7 +1300,17 @@ __device__ __forceinline__ void prefix_and_sample_pairs(const Params& p, const I
     HeadState sB;
     const int nB = setup(hB, sB) ? sB.m_hi - sB.m_lo : 0;
     if (nA <= kFewTargets && nB <= kFewTargets) {
-        sample_pair<G, D, E>(p, it, sA, hA, nA, sB, hB, nB, L, smem, slot_of(hA), slot_of(hB));
+        float* slotA = slot_of(hA);
+        float* slotB = slot_of(hB);
+        sample_pair<G, D, E>(p, it, sA, hA, nA, sB, hB, nB, L, smem,
+                             [&](int col, const float* vals) {
+#pragma unroll
+                                 for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slotA + col + e, vals[e]);
+                             },
+                             [&](int col, const float* vals) {
+#pragma unroll
+                                 for (int e = 0; e < D / 64; ++e) unsafeAtomicAdd(slotB + col + e, vals[e]);
+                             });
     } else {
         if (nA > 0) one_head(sA, hA);
         if (nB > 0) one_head(sB, hB);

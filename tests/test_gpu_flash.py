@@ -34,12 +34,15 @@ def _check(x, S, mode, seed=3, split=0, heads=None):
     return o, idx
 
 
+@pytest.mark.parametrize("G", [4, 7])
 @pytest.mark.parametrize("per_tile", [32, 33])
 @pytest.mark.parametrize("mode", [W.MODE_STRATIFIED, W.MODE_SYSTEMATIC])
-def test_flash_sampler_paths_at_the_few_target_limit(per_tile, mode):
+def test_flash_sampler_paths_at_the_few_target_limit(per_tile, mode, G):
     """Four 512-key tiles with S = 4 * per_tile: each tile samples per_tile
-    targets, one per lane up to 32 and by per-key counts above."""
-    _check(_inputs(lens=(2048,), q_scale=0.0, sinks=0), 4 * per_tile, mode, split=512)
+    targets, one per lane up to 32 and by per-key counts above; with 7 heads
+    on four waves, up to 32 a wave samples its two heads before one gather of
+    both, above that one head after the other."""
+    _check(_inputs(G=G, lens=(2048,), q_scale=0.0, sinks=0), 4 * per_tile, mode, split=512)
 
 
 @pytest.mark.parametrize("mode", [W.MODE_STRATIFIED, W.MODE_SYSTEMATIC])
