@@ -135,16 +135,16 @@ def test_two_stage_calls_equal_decode():
         assert torch.allclose(o1, o2, rtol=1e-5, atol=1e-6)
 
 
-@pytest.mark.parametrize("G", [7, 8])
+@pytest.mark.parametrize("G,dtype,page", [(7, "bf16", 0), (8, "bf16", 0), (7, "bf16", 16), (8, "f32", 32)])
 @pytest.mark.parametrize("mode", [0, 1, 2])
-def test_two_stage_two_heads_per_wave(G, mode):
+def test_two_stage_two_heads_per_wave(G, dtype, page, mode):
     """Groups of 7 and 8 heads on four waves, in the sample pass and in the fused
     kernel: a wave samples two heads and, when each has at most 32 targets in
     its split, gathers both heads' rows in one loop; a dominant sink gives
     splits where a head holds more than that (the one-head-at-a-time gather)
     and splits where a head holds none.  Both paths against the oracle, with
     the same indices."""
-    x = _inputs(G=G, lens=(900, 1200), q_scale=4.0, sinks=1)
+    x = _inputs(G=G, dtype=dtype, lens=(900, 1200), page_size=page, q_scale=4.0, sinks=1)
     o2, i2, _, _ = H.run_hip(x, 256, mode, seed=31, split=128, stages="split")
     print(H.check_all(x, 256, mode, 31, o2, i2))
     o1, i1, _, _ = H.run_hip(x, 256, mode, seed=31, split=128)
