@@ -1,5 +1,6 @@
 import os
 import sys
+import tempfile
 
 import pytest
 
@@ -28,16 +29,15 @@ def golden_dir():
 
 def pytest_sessionfinish(session, exitstatus):
     """Writes the boundary-case counts and worst relative L2 of every GPU parity
-    configuration checked in this session to parity_report.json in the output folder
-    (PARITY_REPORT_DIR, by default the repository's output folder, whose contents a run
-    on another machine brings back)."""
+    configuration checked in this session to parity_report.json in the folder
+    PARITY_REPORT_DIR names (by default the system's temporary folder)."""
     import json
     import sys
     helpers = sys.modules.get("tests.gpu_helpers")
     reports = getattr(helpers, "SESSION_REPORTS", None) if helpers else None
     if not reports:
         return
-    out = os.environ.get("PARITY_REPORT_DIR") or os.path.join(ROOT, "gpurun_out")
+    out = os.environ.get("PARITY_REPORT_DIR") or tempfile.gettempdir()
     os.makedirs(out, exist_ok=True)
     total = dict(configs=len(reports), heads=0, targets=0, boundary_cases=0, boundary_mismatches=0,
                  worst_rel_l2=0.0)
