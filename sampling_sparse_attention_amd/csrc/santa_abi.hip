@@ -210,6 +210,7 @@ santa_status make_params(const santa_shape* s, const void* q, const void* k, con
     p->items = (int32_t)((int64_t)s->batch * s->num_kv_heads * plan->T);
     p->item_order = santa::kOrderSplitFastest;
     p->use_ticket = 0;
+    p->sort_in_score = 0;
     p->kt = nullptr;
     p->kt_stride_seq = p->kt_stride_head = p->kt_stride_feat = 0;
     p->bern_B = 0;
@@ -258,8 +259,15 @@ santa_status run(int stages, const santa_shape* s, const void* q, const void* k,
         if (path == 0) return fail(SANTA_STATUS_HIP_ERROR, "querying the device for the launch plan failed");
     }
     if ((stages & kScore) && mode == SANTA_MODE_MULTINOMIAL) {
-        st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
-        if (st != SANTA_STATUS_OK) return st;
+        // the two-kernel path's score pass sorts the targets itself when its grid
+        // has a workgroup per (sequence, query head) and their LDS holds the sort
+        if (path == 2 && (int64_t)p.items >= (int64_t)p.B * p.Hq &&
+            santa::sort_lds_bytes(S) <= santa::split_lds_bytes(p.G, p.D, p.split, santa::kThreads)) {
+            p.sort_in_score = 1;
+        } else {
+            st = hip_check(santa::launch_targets(p, hs), "launching the target sort");
+            if (st != SANTA_STATUS_OK) return st;
+        }
     }
     if (path == 1 || path == 3) {
         if (path == 1) {

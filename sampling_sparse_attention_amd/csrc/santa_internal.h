@@ -90,6 +90,8 @@ struct Params {
     int32_t items;                // B * Hkv * T work items (one workgroup each)
     int32_t item_order;           // kOrder*: how a workgroup index maps to (b, g, t)
     int32_t use_ticket;           // fused kernel: items taken in start order from sync->ticket
+    int32_t sort_in_score;        // multinomial, two-kernel path: the score pass's first B * Hq
+                                  // workgroups sort the targets (no separate launch)
     int32_t S;
     int32_t mode;
     // Bernoulli qK^T: K transposed ([B, Hkv, d, tokens], tokens contiguous), the

@@ -14,6 +14,48 @@ size_t sort_lds_bytes(int S) {
     return (size_t)n * sizeof(uint64_t);
 }
 
+// Multinomial targets: the S uniforms of (sequence, query head) bh, sorted
+// ascending (bitonic sort of their 53-bit integers in `keys`, sort_lds_bytes(S)
+// of LDS), stored as fp64.  Every thread of the workgroup calls it.
+template <int NT>
+__device__ __forceinline__ void sort_targets(const Params& p, int bh, uint64_t* keys) {
+    const int b = bh / p.Hq;
+    const int h = bh - b * p.Hq;
+    if (seq_len_of(p, b) == 0) return;
+    int N = 1;
+    while (N < p.S) N <<= 1;
+    for (int j = threadIdx.x; j < N; j += NT) {
+        keys[j] = (j < p.S) ? (philox4x64_10_word0((uint64_t)j, (uint64_t)h, (uint64_t)b, 0ull,
+                                                    p.seed, 0ull) >> 11)
+                            : ~0ull;
+    }
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < N; i += NT) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t a = keys[i], c = keys[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((a > c) == up) {
+                        keys[i] = c;
+                        keys[ixj] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    double* dst = p.targets + (int64_t)bh * p.S;
+    for (int j = threadIdx.x; j < p.S; j += NT) dst[j] = (double)keys[j] * 0x1p-53;
+}
+
+// One workgroup per (sequence, query head).
+__global__ __launch_bounds__(256) void targets_kernel(Params p) {
+    extern __shared__ uint64_t keys[];
+    sort_targets<256>(p, blockIdx.x, keys);
+}
+
 // STATS: also the split statistics and records (the sample pass needs them;
 // the top-k comparator reads only the stash).
 template <int G, int D, typename E, int NT, bool STATS>
@@ -40,42 +82,14 @@ __global__ __launch_bounds__(NT) void score_kernel(Params p) {
         write_stash<G, NT, STATS>(p, it, sc);
         if constexpr (STATS) publish_group_prefix<G, NT>(p, it);
     }
-}
-
-// Multinomial targets: the S uniforms of every (sequence, query head), sorted
-// ascending (bitonic sort of their 53-bit integers in LDS), stored as fp64.
-__global__ __launch_bounds__(256) void targets_kernel(Params p) {
-    extern __shared__ uint64_t keys[];
-    const int bh = blockIdx.x;
-    const int b = bh / p.Hq;
-    const int h = bh - b * p.Hq;
-    if (seq_len_of(p, b) == 0) return;
-    int N = 1;
-    while (N < p.S) N <<= 1;
-    for (int j = threadIdx.x; j < N; j += 256) {
-        keys[j] = (j < p.S) ? (philox4x64_10_word0((uint64_t)j, (uint64_t)h, (uint64_t)b, 0ull,
-                                                    p.seed, 0ull) >> 11)
-                            : ~0ull;
-    }
-    __syncthreads();
-    for (int k = 2; k <= N; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < N; i += 256) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint64_t a = keys[i], c = keys[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > c) == up) {
-                        keys[i] = c;
-                        keys[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
+    if constexpr (STATS) {
+        // the first B * Hq workgroups, dispatched first, sort the multinomial
+        // targets once their own split is done, while the others stream K
+        if (p.sort_in_score && blockIdx.x < p.B * p.Hq) {
+            __syncthreads();        // the split's LDS is free again
+            sort_targets<NT>(p, blockIdx.x, reinterpret_cast<uint64_t*>(smem));
         }
     }
-    double* dst = p.targets + (int64_t)bh * p.S;
-    for (int j = threadIdx.x; j < p.S; j += 256) dst[j] = (double)keys[j] * 0x1p-53;
 }
 
 // Zero-fills `n16` 16-byte words and `tail` further bytes.

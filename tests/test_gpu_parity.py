@@ -159,6 +159,21 @@ def test_two_stage_two_heads_per_wave(G, dtype, page, mode):
     assert int((counts == 0).sum()) > 0
 
 
+@pytest.mark.parametrize("G,lens,split", [(8, (40, 50), 64), (4, (3000, 2500), 64), (7, (900, 1200), 128)])
+def test_two_stage_multinomial_target_sort(G, lens, split):
+    """Multinomial targets on the two-kernel path: sorted by the score pass's
+    first B * Hq workgroups when its grid has that many (many splits), by a
+    launch of their own otherwise (one split per sequence, B * Hkv < B * Hq
+    workgroups).  The indices equal the fused path's and the oracle's."""
+    x = _inputs(G=G, lens=lens)
+    o2, i2, ws, _ = H.run_hip(x, 200, 0, seed=13, split=split, stages="split")
+    print(H.check_all(x, 200, 0, 13, o2, i2))
+    assert santa.workspace_error(ws) == 0 and torch.count_nonzero(ws) == 0
+    o1, i1, _, _ = H.run_hip(x, 200, 0, seed=13, split=split)
+    assert torch.equal(i1, i2)
+    assert torch.allclose(o1, o2, rtol=1e-5, atol=1e-6)
+
+
 def test_indices_deterministic_and_split_invariant():
     x = _inputs(lens=(3000, 2500))
     for mode in (0, 1, 2):
